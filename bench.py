@@ -1,0 +1,267 @@
+"""Benchmark of the W6A6 / W6A8 linear-layer path on LLaMA-2-70B shapes, one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input: for every
+token count M in {1, 16, 64, 256, 1024, 4096}, both activation precisions (A6, A8)
+and the four linear layers of a LLaMA-2-70B decoder block (qkv 10240x8192,
+o 8192x8192, gate_up 57344x8192, down 8192x28672), quantize the fp16 activations
+(flexq_quant_act) and run the W6Ax GEMM (flexq_gemm_w6ax) on packed 6-bit weights
+resident in HBM.  Weights are packed once, before timing (offline step).
+
+Prints one JSON line: value = whole-step GEMM+quant throughput in TOPS (2*M*N*K
+integer ops per GEMM, M unpadded), per-shape TOPS / GB/s / roofline fractions,
+the roofline of the dominant kernel and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "W6A6/W6A8 GEMM TOPS + HBM GB/s (% roofline), LLaMA-2-70B linear shapes"
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+GROUP = 128
+LAYERS = synth.LLAMA2_70B
+M_LIST = (1, 16, 64, 256, 1024, 4096)
+ABITS = (6, 8)
+DECODE_MAX_M = 64
+
+
+def gemm_bytes(M, N, K):
+    """Algorithmic HBM bytes of one GEMM: packed W + fp16 s_w + int8 q_a + fp32 s_a + fp16 Y."""
+    G = K // GROUP
+    return 0.75 * N * K + 2 * N * G + M * K + 4 * M * G + 2 * M * N
+
+
+def quant_bytes(M, K):
+    """fp16 X in, int8 q_a + fp32 s_a out."""
+    return 2 * M * K + M * K + 4 * M * (K // GROUP)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--seed", type=int, default=synth.BASE_SEED)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-cols", type=int, default=128,
+                   help="output columns per GEMM in the oracle's timed sample")
+    p.add_argument("--m", type=str, default=None, help="comma list overriding the token counts")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import w6a6_w6a8_integer_amd as fq
+
+    fq.lib()
+    dev = torch.device("cuda:0")
+    m_list = tuple(int(v) for v in args.m.split(",")) if args.m else M_LIST
+    nthreads = synth.default_threads()
+
+    # ---- weights: generated on the host, packed on the GPU, two resident copies
+    # (alternated between passes so no layer is served from the 256 MB MALL)
+    t0 = time.time()
+    packed = {}
+    for li, (name, (N, K)) in enumerate(LAYERS.items()):
+        w = synth.weights(synth.derive_seed(args.seed, "70b", name, "w"), N, K, nthreads=nthreads)
+        wd = torch.from_numpy(w).to(dev)
+        del w
+        copies = []
+        for c in range(2):
+            copies.append(fq.pack_w6(wd))
+        del wd
+        packed[name] = copies
+    torch.cuda.synchronize()
+    log(f"weights packed ({time.time() - t0:.1f} s)")
+
+    # ---- activations and outputs per (M, layer)
+    bufs = {}
+    for M in m_list:
+        for name, (N, K) in LAYERS.items():
+            x = synth.activations(synth.derive_seed(args.seed, "70b", name, "x", M), M, K,
+                                  nthreads=nthreads)
+            xd = torch.from_numpy(x).to(dev)
+            qa = torch.empty((M, K), dtype=torch.int8, device=dev)
+            sa = torch.empty((M, K // GROUP), dtype=torch.float32, device=dev)
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            bufs[(M, name)] = (x, xd, qa, sa, y)
+    torch.cuda.synchronize()
+    log(f"activations ready ({time.time() - t0:.1f} s)")
+
+    plan = [(M, ab, name) for M in m_list for ab in ABITS for name in LAYERS]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in plan]
+
+    def step(timed: bool, s: int):
+        for i, (M, ab, name) in enumerate(plan):
+            N, K = LAYERS[name]
+            _, xd, qa, sa, y = bufs[(M, name)]
+            wp, sw = packed[name][(s * len(plan) + i) % 2]
+            if timed:
+                ev[i][0].record()
+            fq.quant_act(xd, ab, q_a=qa, s_a=sa)
+            if timed:
+                ev[i][1].record()
+            fq.gemm_w6ax(qa, sa, wp, sw, N, ab, y=y)
+            if timed:
+                ev[i][2].record()
+
+    for s in range(args.warmup):
+        step(False, s)
+    torch.cuda.synchronize()
+
+    quant_ms = {k: [] for k in plan}
+    gemm_ms = {k: [] for k in plan}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_ms = []
+    torch.cuda.synchronize()
+    wall0 = time.time()
+    start.record()
+    for s in range(args.steps):
+        step(True, s)
+        torch.cuda.synchronize()  # read this step's events; the region stays back to back
+        for i, k in enumerate(plan):
+            quant_ms[k].append(ev[i][0].elapsed_time(ev[i][1]))
+            gemm_ms[k].append(ev[i][1].elapsed_time(ev[i][2]))
+        step_ms.append(ev[0][0].elapsed_time(ev[-1][2]))
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    total_ms = start.elapsed_time(stop)
+
+    # ---- aggregate
+    shapes = []
+    tot_ops = 0.0
+    dec_ops = dec_bytes = dec_ms = 0.0
+    pre_ops = pre_ms = 0.0
+    for k in plan:
+        M, ab, name = k
+        N, K = LAYERS[name]
+        g = statistics.median(gemm_ms[k])
+        q = statistics.median(quant_ms[k])
+        ops = 2.0 * M * N * K
+        by = gemm_bytes(M, N, K)
+        tot_ops += ops
+        gsum = sum(gemm_ms[k])
+        if M <= DECODE_MAX_M:
+            dec_ops += ops * len(gemm_ms[k])
+            dec_bytes += by * len(gemm_ms[k])
+            dec_ms += gsum
+        else:
+            pre_ops += ops * len(gemm_ms[k])
+            pre_ms += gsum
+        shapes.append({
+            "layer": name, "M": M, "N": N, "K": K, "abits": ab,
+            "kernel": "decode" if M <= DECODE_MAX_M else "prefill",
+            "gemm_us": round(g * 1e3, 2), "quant_us": round(q * 1e3, 2),
+            "tops": round(ops / (g * 1e-3) / 1e12, 2),
+            "gbs": round(by / (g * 1e-3) / 1e9, 1),
+            "frac_hbm": round(by / (g * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+            "frac_int8": round(ops / (g * 1e-3) / 1e12 / INT8_PEAK_TOPS, 3),
+            "quant_gbs": round(quant_bytes(M, K) / (q * 1e-3) / 1e9, 1),
+        })
+    ms_per_step = statistics.median(step_ms)
+    value = tot_ops / (ms_per_step * 1e-3) / 1e12
+
+    pre_tops = pre_ops / (pre_ms * 1e-3) / 1e12 if pre_ms else 0.0
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9 if dec_ms else 0.0
+    if pre_ms >= dec_ms:
+        roofline = {"kernel": "gemm_prefill_kernel", "bound": "mfma", "achieved": round(pre_tops, 1),
+                    "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(pre_tops / INT8_PEAK_TOPS, 4),
+                    "traffic": None}
+    else:
+        roofline = {"kernel": "gemm_decode_kernel", "bound": "hbm", "achieved": round(dec_gbs, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": None}
+    roofline_decode = {"kernel": "gemm_decode_kernel", "bound": "hbm", "achieved": round(dec_gbs, 1),
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(bufs, m_list, args.cpu_sample_cols, packed, ms_per_step, tot_ops)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "llama2_70b_linear_layers_w6a6_w6a8",
+                   "layers": {k: list(v) for k, v in LAYERS.items()}, "M": list(m_list),
+                   "abits": list(ABITS), "group": GROUP, "step": "quant_act + gemm per (M, abits, layer)"},
+        "roofline": roofline, "roofline_decode": roofline_decode,
+        "cpu_baseline": cpu,
+        "timed_region_ms": round(total_ms, 2), "wall_s": round(wall, 2),
+        "shapes": shapes,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(bufs, m_list, cols, packed, gpu_ms_per_step, tot_ops):
+    """The oracle, as it is, on a bounded sample of the same step: full activation
+    quantization of every (M, layer) input, and every GEMM restricted to its first
+    `cols` output columns; the GEMM time is scaled linearly in N (exact: the work
+    is linear in N) to estimate the oracle's time for the whole step."""
+    import oracle
+    import torch
+
+    threads = synth.default_threads()
+    q_time = 0.0
+    g_time = 0.0
+    g_time_scaled = 0.0
+    sample_ops = 0.0
+    wq = {}
+    for name, (N, K) in LAYERS.items():
+        wp, sw = packed[name][0]
+        n = min(cols, N)
+        wps = wp[: n * K * 3 // 16].cpu().numpy().view(np.uint32)  # first n/16 tiles
+        sws = sw[:n].cpu().numpy()
+        wq[name] = (oracle.unpack_codes(wps, n, K), sws, n)
+    for M in m_list:
+        for ab in ABITS:
+            for name, (N, K) in LAYERS.items():
+                x = bufs[(M, name)][0]
+                t = time.perf_counter()
+                qa, sa = oracle.quant_act(x, ab)
+                q_time += time.perf_counter() - t
+                qw, sws, n = wq[name]
+                t = time.perf_counter()
+                oracle.gemm(qa, sa, qw, sws, nthreads=threads)
+                dt = time.perf_counter() - t
+                g_time += dt
+                g_time_scaled += dt * (N / n)
+                sample_ops += 2.0 * M * n * K
+    est_step_s = q_time + g_time_scaled
+    return {"value": round(tot_ops / est_step_s / 1e12, 5), "unit": "TOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"every (M, abits, layer) of the step: full activation quantization "
+                       f"({q_time:.1f} s, 1 thread) and the GEMM on the first {cols} output "
+                       f"columns ({g_time:.1f} s, {threads} threads), GEMM time scaled by N/{cols}; "
+                       f"estimated oracle step {est_step_s:.0f} s vs GPU {gpu_ms_per_step:.2f} ms"),
+            "sample_cpu_s": round(q_time + g_time, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * flexq.h -- C ABI of the MI355X (gfx950) W6A6 / W6A8 group-quantized linear layer.
+ *
+ * The method is FlexQ (arXiv 2508.04405, "FlexQ: Efficient Post-training INT6
+ * Quantization for LLM Serving via Algorithm-System Co-Design"):
+ *   - abstract: uniform 6-bit weights in every layer; activations kept at 6 bits
+ *     in most layers and at 8 bits in sensitive ones; a kernel for the W6A6 and
+ *     W6A8 matrix multiply;
+ *   - blog "Six-bit frontier", section "Fine-Grained Quantization and Layer
+ *     Sensitivity": weights and activations are split into small groups that
+ *     share one scale factor;
+ *   - same blog, section "Bridging Software and Hardware with BTC": the groups run
+ *     along K (128 deep), every group yields an exact integer partial product, and
+ *     the dequantization is fused into the GEMM.
+ *
+ * All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) and
+ * are owned by the caller; the library allocates no memory the caller sees.
+ * `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call
+ * validates its arguments on the host first; on error it returns without touching
+ * the GPU.  On success the work is enqueued and the call returns; a fault during
+ * execution surfaces at the caller's next synchronisation, as in HIP.
+ *
+ * Layouts (row-major, contiguous):
+ *   W   fp16 [N][K]         nn.Linear weight ([out][in]); Y = X * W^T
+ *   X   fp16 [M][K]         activations, one row per token
+ *   q_a int8 [M][K]         quantized activations (one code per byte)
+ *   s_a fp32 [M][K/128]     activation scales
+ *   s_w fp16 [N][K/128]     weight scales
+ *   w_packed                6-bit weight codes, 16 codes per 3 dwords:
+ *       v = q & 63, lo = v & 15, hi = v >> 4 (q in [-31, 31]; -32 decodes but is
+ *       never produced), for byte j = 0..3 of each dword:
+ *         dword0.byte[j] = lo[j]   | lo[4+j]  << 4
+ *         dword1.byte[j] = lo[8+j] | lo[12+j] << 4
+ *         dword2.byte[j] = hi[j] | hi[4+j] << 2 | hi[8+j] << 4 | hi[12+j] << 6
+ *       (a 4-bit plane plus a 2-bit plane, the 4+2 split of ZeroQuant(4+2)).
+ *       The unit of rows n, codes k = 16u .. 16u+15 starts at dword
+ *         3 * (((n / 16) * (K / 16) + u) * 16 + n % 16),
+ *       i.e. 16-row tiles, unit index major, row-in-tile minor.
+ *   Y   fp16 [M][N]
+ *
+ * Quantizers (symmetric, round half to even, IEEE binary32 division):
+ *   weights, per (n, group g):    amax = max |w|;  s16 = fp16(amax / 31)  (0 if amax = 0);
+ *                                 q = clamp(rint(w / float(s16)), -31, 31)  (0 if s16 = 0)
+ *   activations, per (m, g):      amax = max |x|;  s = amax / qmax in fp32 (0 if amax = 0);
+ *                                 q = clamp(rint(x / s), -qmax, qmax), qmax = 31 (A6) or 127 (A8)
+ * Product:
+ *   d[m][n][g] = sum_{k in g} q_a[m][k] * q_w[n][k]           (exact int32)
+ *   acc = +0;  for g ascending:  t = RN32(float(d) * float(s_w[n][g]));
+ *                                acc = fma(t, s_a[m][g], acc)
+ *   Y[m][n] = fp16(acc).
+ *
+ * Preconditions: finite inputs; outputs must not overlap inputs; group_size == 128;
+ * K a positive multiple of 128; N a multiple of 16; pointers aligned as stated.
+ * The functions keep no mutable global state and may be called from any thread.
+ */
+#ifndef FLEXQ_H
+#define FLEXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLEXQ_SUCCESS = 0,
+  FLEXQ_ERROR_INVALID_VALUE = 1, /* null pointer, negative size, abits not 6/8, overlap */
+  FLEXQ_ERROR_UNSUPPORTED = 2,   /* group_size != 128, K % 128 != 0, N % 16 != 0, misalignment */
+  FLEXQ_ERROR_LAUNCH = 3         /* the HIP runtime rejected a launch */
+} flexq_status;
+
+typedef enum {
+  FLEXQ_PATH_AUTO = 0,    /* decode for M <= FLEXQ_DECODE_MAX_M, prefill above */
+  FLEXQ_PATH_DECODE = 1,  /* HBM-streaming kernel for few tokens (any M is accepted) */
+  FLEXQ_PATH_PREFILL = 2  /* MFMA-bound tiled kernel for many tokens (any M is accepted) */
+} flexq_path;
+
+#define FLEXQ_ABI_VERSION 1
+#define FLEXQ_PACK_FORMAT_VERSION 1
+#define FLEXQ_GROUP_SIZE 128
+#define FLEXQ_DECODE_MAX_M 64
+
+/* FLEXQ_ABI_VERSION of the loaded library. */
+int flexq_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* flexq_status_string(flexq_status status);
+
+/* Bytes of w_packed for an N x K weight: 0.75 * N * K (12 bytes per 16 codes).
+   Returns 0 for N <= 0, K <= 0 or K not a multiple of 16. */
+size_t flexq_packed_w6_bytes(int64_t N, int64_t K);
+
+/* Weight group quantization and packing (offline; FlexQ abstract: uniform 6-bit
+   weights; blog, "Fine-Grained Quantization ...": one scale per group).
+     w_fp16   [N][K] fp16 bits, 16-byte aligned          (input)
+     w_packed flexq_packed_w6_bytes(N, K) bytes, 16-byte aligned (output)
+     s_w_fp16 [N][K/128] fp16 bits, 2-byte aligned        (output)
+   N == 0 is a no-op.  Errors: INVALID_VALUE (null, N < 0, K <= 0, overlap),
+   UNSUPPORTED (group_size != 128, K % 128, N % 16, alignment). */
+flexq_status flexq_pack_w6(const uint16_t* w_fp16, int64_t N, int64_t K, int32_t group_size,
+                           uint32_t* w_packed, uint16_t* s_w_fp16, void* stream);
+
+/* Per-token, per-group symmetric activation quantization to INT6 (abits = 6) or
+   INT8 (abits = 8) (blog, "Fine-Grained Quantization ...": 6-bit activations in most
+   layers, 8-bit in sensitive ones).
+     x_fp16 [M][K] fp16 bits, 16-byte aligned (input)
+     q_a    [M][K] int8, 8-byte aligned       (output)
+     s_a    [M][K/128] fp32, 4-byte aligned   (output)
+   M == 0 is a no-op.  Errors as for flexq_pack_w6, plus INVALID_VALUE for abits. */
+flexq_status flexq_quant_act(const uint16_t* x_fp16, int64_t M, int64_t K, int32_t group_size,
+                             int32_t abits, int8_t* q_a, float* s_a, void* stream);
+
+/* Y = sum over groups of int32 group dot x s_w x s_a, fp32 accumulation, fp16 out
+   (blog, "Bridging Software and Hardware with BTC": exact integer group products,
+   dequantization fused into the GEMM).  The result is bit-identical to the formula
+   in this header's preamble on every path.
+     q_a      [M][K] int8, 16-byte aligned     s_a [M][K/128] fp32, 4-byte aligned
+     w_packed packed codes, 16-byte aligned   s_w [N][K/128] fp16, 2-byte aligned
+     y_fp16   [M][N] fp16, 4-byte aligned (output)
+   abits (6 or 8) is validated; both are stored as int8 so the product is the same.
+   M == 0 or N == 0 is a no-op. */
+flexq_status flexq_gemm_w6ax(const int8_t* q_a, const float* s_a, const uint32_t* w_packed,
+                             const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K,
+                             int32_t group_size, int32_t abits, uint16_t* y_fp16, void* stream);
+
+/* flexq_gemm_w6ax with an explicit kernel choice (flexq_path); both kernels accept
+   every M and give identical results. */
+flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a,
+                                  const uint32_t* w_packed, const uint16_t* s_w_fp16,
+                                  int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                  int32_t abits, int32_t path, uint16_t* y_fp16, void* stream);
+
+/* The int32 group dots d[m][n][g] (the integer products of the BTC section) computed
+   with the same weight unpack and int8 MFMA as the GEMM; for verification.
+     dots [M][N][K/128] int32, 4-byte aligned (output). */
+flexq_status flexq_gemm_w6ax_group_dots(const int8_t* q_a, const uint32_t* w_packed,
+                                        int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                        int32_t* dots, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLEXQ_H */

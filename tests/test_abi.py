@@ -1,0 +1,139 @@
+"""The C-ABI library loads on the CPU, exports every symbol include/flexq.h declares,
+and rejects bad arguments on the host before any HIP call (no kernel runs here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flexq.h")
+LIB = os.path.join(ROOT, "w6a6_w6a8_integer_amd", "libflexq.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libflexq.so not built")
+
+SUCCESS, INVALID, UNSUPPORTED, LAUNCH = 0, 1, 2, 3
+A16 = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced on error paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flexq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def flexq():
+    import torch  # noqa: F401  (the HIP runtime must be the one torch loads)
+    import w6a6_w6a8_integer_amd as fq
+    return fq.lib()
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ["flexq_pack_w6", "flexq_quant_act", "flexq_gemm_w6ax"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(flexq):
+    out = subprocess.check_output(["nm", "-D", "--defined-only", LIB]).decode()
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    import w6a6_w6a8_integer_amd as fq
+    assert set(declared_functions()) == set(fq.SIGNATURES)
+
+
+def test_versions_and_status_strings(flexq):
+    assert flexq.flexq_abi_version() == 1
+    for s in range(4):
+        assert flexq.flexq_status_string(s).decode().startswith("FLEXQ_")
+    assert b"unknown" in flexq.flexq_status_string(99)
+    assert flexq.flexq_packed_w6_bytes(4096, 4096) == 4096 * 4096 * 3 // 4
+    assert flexq.flexq_packed_w6_bytes(16, 8) == 0
+    assert flexq.flexq_packed_w6_bytes(0, 128) == 0
+
+
+def test_pack_w6_rejects_bad_arguments(flexq):
+    f = flexq.flexq_pack_w6
+    assert f(None, 16, 128, 128, 2 * A16, 3 * A16, None) == INVALID
+    assert f(A16, 16, 128, 128, None, 3 * A16, None) == INVALID
+    assert f(A16, -16, 128, 128, 2 * A16, 3 * A16, None) == INVALID
+    assert f(A16, 16, 0, 128, 2 * A16, 3 * A16, None) == INVALID
+    assert f(A16, 16, 128, 64, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert f(A16, 16, 192, 128, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert f(A16, 24, 128, 128, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert f(A16 + 8, 16, 128, 128, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert f(A16, 16, 128, 128, 2 * A16 + 4, 3 * A16, None) == UNSUPPORTED
+    # output overlapping the input
+    assert f(A16, 16, 128, 128, A16 + 16, 3 * A16, None) == INVALID
+    # empty weight: nothing to do, no pointer is looked at
+    assert f(None, 0, 128, 128, None, None, None) == SUCCESS
+
+
+def test_quant_act_rejects_bad_arguments(flexq):
+    f = flexq.flexq_quant_act
+    assert f(A16, 4, 128, 128, 7, 2 * A16, 3 * A16, None) == INVALID
+    assert f(None, 4, 128, 128, 6, 2 * A16, 3 * A16, None) == INVALID
+    assert f(A16, 4, 128, 128, 6, 2 * A16, None, None) == INVALID
+    assert f(A16, -1, 128, 128, 6, 2 * A16, 3 * A16, None) == INVALID
+    assert f(A16, 4, 100, 128, 6, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert f(A16, 4, 128, 32, 8, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert f(A16 + 2, 4, 128, 128, 6, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert f(A16, 4, 128, 128, 6, 2 * A16 + 4, 3 * A16, None) == UNSUPPORTED
+    assert f(A16, 4, 128, 128, 6, 2 * A16, 3 * A16 + 2, None) == UNSUPPORTED
+    assert f(A16, 4, 128, 128, 6, A16 + 256, 3 * A16, None) == INVALID  # q_a inside x
+    assert f(None, 0, 128, 128, 8, None, None, None) == SUCCESS
+    assert f(A16, 1 << 21, 128, 128, 6, 2 * A16, 3 * A16, None) == UNSUPPORTED  # M limit
+
+
+def test_gemm_rejects_bad_arguments(flexq):
+    f = flexq.flexq_gemm_w6ax
+    g = flexq.flexq_gemm_w6ax_path
+    args = dict(qa=A16, sa=2 * A16, wp=3 * A16, sw=4 * A16, y=5 * A16)
+
+    def call(M=4, N=16, K=128, group=128, abits=6, **kw):
+        a = {**args, **kw}
+        return f(a["qa"], a["sa"], a["wp"], a["sw"], M, N, K, group, abits, a["y"], None)
+
+    assert call(abits=4) == INVALID
+    assert call(qa=None) == INVALID
+    assert call(sa=None) == INVALID
+    assert call(wp=None) == INVALID
+    assert call(sw=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(M=-1) == INVALID
+    assert call(N=-16) == INVALID
+    assert call(K=0) == INVALID
+    assert call(K=130) == UNSUPPORTED
+    assert call(N=24) == UNSUPPORTED
+    assert call(group=256) == UNSUPPORTED
+    assert call(qa=A16 + 8) == UNSUPPORTED
+    assert call(wp=3 * A16 + 4) == UNSUPPORTED
+    assert call(sa=2 * A16 + 2) == UNSUPPORTED
+    assert call(y=5 * A16 + 2) == UNSUPPORTED
+    assert call(y=A16 + 64) == INVALID  # Y overlaps q_a
+    assert call(y=3 * A16 + 32) == INVALID  # Y overlaps the packed weight
+    assert call(M=0, qa=None, y=None) == SUCCESS
+    assert call(N=0, wp=None, y=None) == SUCCESS
+    assert g(A16, 2 * A16, 3 * A16, 4 * A16, 4, 16, 128, 128, 6, 7, 5 * A16, None) == INVALID
+
+
+def test_group_dots_rejects_bad_arguments(flexq):
+    f = flexq.flexq_gemm_w6ax_group_dots
+    assert f(None, 2 * A16, 4, 16, 128, 128, 3 * A16, None) == INVALID
+    assert f(A16, 2 * A16, 4, 16, 128, 128, None, None) == INVALID
+    assert f(A16, 2 * A16, 4, 16, 128, 64, 3 * A16, None) == UNSUPPORTED
+    assert f(A16, 2 * A16, 4, 16, 128, 128, 3 * A16 + 1, None) == UNSUPPORTED
+    assert f(A16, 2 * A16, 4, 16, 128, 128, A16, None) == INVALID
+    assert f(None, None, 0, 16, 128, 128, None, None) == SUCCESS
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import w6a6_w6a8_integer_amd as fq
+    with pytest.raises(TypeError):
+        fq.pack_w6(torch.zeros(16, 128, dtype=torch.float16))
+    with pytest.raises(TypeError):
+        fq.quant_act(torch.zeros(2, 128, dtype=torch.float16), 6)

@@ -1,0 +1,170 @@
+// gemm_decode.hip -- W6Ax GEMM for few tokens (M <= 64): an HBM-streaming kernel.
+//
+// FlexQ blog, "Bridging Software and Hardware with BTC": K is cut into 128-deep
+// groups, each group gives an exact integer product, partial results are
+// reduced and the dequantization is fused; the kernel is meant to use the
+// memory hierarchy well at small batch.  On gfx950 the integer product is an
+// int8 MFMA (v_mfma_i32_16x16x64_i8) over weights unpacked in registers, and
+// the time goes to streaming the 0.75 B/weight packed matrix from HBM.
+//
+// Work split: one workgroup per 16-column tile of W, S waves.  Round r hands
+// group g = r*S + w to wave w, so a round reads S*1536 contiguous bytes of the
+// tile.  Every wave keeps P rounds of loads in flight (weights, activations and
+// both scales, issued together so the in-order vmcnt never waits on a younger
+// load).  After its two MFMAs a wave parks the 16 x rows int32 dots and the
+// group's scales in LDS; after one barrier the block folds the S groups into
+// the fp32 accumulators in ascending group order, so the result equals the
+// sequential definition bit for bit.
+#include "kernels.h"
+#include "w6_device.h"
+
+namespace flexq {
+
+namespace {
+
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw 32-bit dword buffer, gfx9 style
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
+template <int MT>
+struct Bundle {
+  u32x3 w[2];       // two weight units (k-blocks of 64)
+  i32x4 a[MT][2];   // activation fragments, rows ms*16 + lane%16
+  float sa;         // s_a[row = lane][g]
+  uint32_t sw;      // s_w[col = lane%16][g] (fp16 bits)
+};
+
+}  // namespace
+
+template <int MT, int S, int P>
+__global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
+    const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint32_t* __restrict__ wp,
+    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ y) {
+  static_assert(P % 2 == 0, "slot parity must be static");
+  constexpr int ROWS = MT * 16;
+  constexpr int OUTS = ROWS * 16;
+  constexpr int THREADS = 64 * S;
+  constexpr int OPT = (OUTS + THREADS - 1) / THREADS;
+
+  const int G = K >> 7;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x;
+  const int row0 = blockIdx.y * 64;
+  const int rows = min(ROWS, M - row0);  // >= 1
+  const int R = (G + S - 1) / S;
+  const int Rp = (R + P - 1) / P * P;
+
+  // Out-of-range buffer loads return zero: rows >= `rows` and groups >= G vanish.
+  const auto rw = make_rsrc(wp + (size_t)tile * 3 * K, 12u * (uint32_t)K);
+  const auto ra = make_rsrc(qa + (size_t)row0 * K, (uint32_t)rows * (uint32_t)K);
+  const auto rsa = make_rsrc(sa + (size_t)row0 * G, (uint32_t)rows * (uint32_t)G * 4u);
+  const auto rsw = make_rsrc(sw + (size_t)tile * 16 * G, 32u * (uint32_t)G);
+
+  __shared__ int32_t lds_d[2][S][OUTS];
+  __shared__ float lds_sa[2][S][ROWS];
+  __shared__ float lds_sw[2][S][16];
+
+  const uint32_t a_lane_off = (uint32_t)(lane & 15) * (uint32_t)K + (uint32_t)(lane >> 4) * 16u;
+
+  auto load = [&](Bundle<MT>& b, int r) {
+    const uint32_t g = (uint32_t)(r * S + wave);
+    b.w[0] = __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + lane) * 12u, 0, 0);
+    b.w[1] = __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + 64u + lane) * 12u, 0, 0);
+#pragma unroll
+    for (int ms = 0; ms < MT; ++ms) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b.a[ms][j] = __builtin_amdgcn_raw_buffer_load_b128(
+            ra, a_lane_off + (uint32_t)(ms * 16) * (uint32_t)K + g * 128u + j * 64u, 0, 0);
+    }
+    b.sa = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rsa, ((uint32_t)lane * G + g) * 4u, 0, 0));
+    b.sw = __builtin_amdgcn_raw_buffer_load_b16(rsw, ((uint32_t)(lane & 15) * G + g) * 2u, 0, 0);
+  };
+
+  Bundle<MT> ring[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) load(ring[p], p);
+
+  float acc[OPT];
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) acc[i] = 0.0f;
+
+  const i32x4 zero = {0, 0, 0, 0};
+  for (int r0 = 0; r0 < Rp; r0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int r = r0 + p;
+      const int slot = p & 1;
+      Bundle<MT>& b = ring[p];
+      // exact integer group products (4*d, see w6_device.h)
+      const i32x4 b0 = unpack_unit_x4(b.w[0][0], b.w[0][1], b.w[0][2]);
+      const i32x4 b1 = unpack_unit_x4(b.w[1][0], b.w[1][1], b.w[1][2]);
+      i32x4 d[MT];
+#pragma unroll
+      for (int ms = 0; ms < MT; ++ms) {
+        d[ms] = mfma16(b.a[ms][0], b0, zero);
+        d[ms] = mfma16(b.a[ms][1], b1, d[ms]);
+      }
+      // park dots (row-major [row][col]) and this group's scales
+#pragma unroll
+      for (int ms = 0; ms < MT; ++ms)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          lds_d[slot][wave][(ms * 16 + 4 * (lane >> 4) + i) * 16 + (lane & 15)] = d[ms][i];
+      if (lane < ROWS) lds_sa[slot][wave][lane] = b.sa;
+      if (lane < 16) lds_sw[slot][wave][lane] = half_bits_to_float((uint16_t)b.sw);
+      load(b, r + P);
+      __syncthreads();
+      // fold the S groups of this round, ascending g
+      const int gbase = r * S;
+      const int ng = min(S, G - gbase);
+#pragma unroll
+      for (int i = 0; i < OPT; ++i) {
+        const int o = threadIdx.x + i * THREADS;
+        if (o < OUTS && (o >> 4) < rows) {
+          const int row = o >> 4, col = o & 15;
+          float a = acc[i];
+          for (int w = 0; w < ng; ++w) {
+            const float t = (float)(lds_d[slot][w][o] >> 2) * lds_sw[slot][w][col];
+            a = fmaf(t, lds_sa[slot][w][row], a);
+          }
+          acc[i] = a;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) {
+    const int o = threadIdx.x + i * THREADS;
+    if (o < OUTS && (o >> 4) < rows)
+      y[(size_t)(row0 + (o >> 4)) * N + (size_t)tile * 16 + (o & 15)] = float_to_half_bits(acc[i]);
+  }
+}
+
+template <int MT, int S, int P>
+static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint32_t* wp,
+                                  const uint16_t* sw, int64_t M, int64_t N, int64_t K,
+                                  uint16_t* y, hipStream_t stream) {
+  dim3 grid((unsigned)(N / 16), (unsigned)((M + 63) / 64));
+  hipLaunchKernelGGL((gemm_decode_kernel<MT, S, P>), grid, dim3(64 * S), 0, stream, qa, sa, wp,
+                     sw, (int)M, (int)N, (int)K, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t* wp,
+                              const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                              hipStream_t stream) {
+  // rows per pass: 16 * MT; more passes over W only when M > 64
+  const int64_t rows = M > 64 ? 64 : M;
+  if (rows <= 16) return launch_decode_t<1, 8, 8>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 32) return launch_decode_t<2, 8, 6>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 48) return launch_decode_t<3, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
+  return launch_decode_t<4, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
+}
+
+}  // namespace flexq

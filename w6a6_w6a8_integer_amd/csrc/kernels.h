@@ -1,0 +1,30 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (internal to libflexq).
+// Arguments are already validated by the C ABI layer (api.hip) when these run.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flexq {
+
+hipError_t launch_pack_w6(const uint16_t* w, int64_t N, int64_t K, uint32_t* wp, uint16_t* sw,
+                          hipStream_t stream);
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int qmax, int8_t* qa,
+                            float* sa, hipStream_t stream);
+
+hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t* wp,
+                              const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                              hipStream_t stream);
+
+hipError_t launch_gemm_prefill(const int8_t* qa, const float* sa, const uint32_t* wp,
+                               const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                               hipStream_t stream);
+
+hipError_t launch_group_dots(const int8_t* qa, const uint32_t* wp, int64_t M, int64_t N,
+                             int64_t K, int32_t* dots, hipStream_t stream);
+
+// Largest M the decode kernel handles in one pass (rows are processed in
+// passes of this many tokens above it).
+constexpr int64_t kDecodeRowsPerPass = 64;
+
+}  // namespace flexq

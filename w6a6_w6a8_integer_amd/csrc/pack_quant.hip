@@ -1,0 +1,115 @@
+// pack_quant.hip -- weight group quantization + 6-bit packing, and activation
+// group quantization (FlexQ blog, "Fine-Grained Quantization and Layer
+// Sensitivity": one scale per small group of weights or activations; FlexQ
+// abstract: 6-bit weights everywhere, 6- or 8-bit activations per layer).
+//
+// Both kernels are HBM-bound elementwise passes.  Arithmetic follows the
+// formulas of the public header exactly (IEEE division, round half to even),
+// so their outputs are bit-identical to the plain definition.
+#include "kernels.h"
+#include "w6_device.h"
+
+namespace flexq {
+
+// One workgroup = one 16-row tile x one 128-deep group.  Thread t handles row
+// t/8 of the tile and unit t%8 of the group (16 codes); the 8 threads of a row
+// are adjacent lanes, so the group max is a 3-step butterfly.
+__global__ __launch_bounds__(128) void pack_w6_kernel(const uint16_t* __restrict__ w, int K,
+                                                      uint32_t* __restrict__ wp,
+                                                      uint16_t* __restrict__ sw) {
+  const int G = K >> 7;
+  const int t = threadIdx.x;
+  const int r = t >> 3, j = t & 7;
+  const int64_t n = (int64_t)blockIdx.x * 16 + r;
+  const int g = blockIdx.y;
+  const u32x4* src = reinterpret_cast<const u32x4*>(w + n * K + g * kGroup + j * 16);
+  u32x4 h0 = src[0], h1 = src[1];
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = half_bits_to_float((uint16_t)(h0[i] & 0xFFFFu));
+    v[2 * i + 1] = half_bits_to_float((uint16_t)(h0[i] >> 16));
+    v[8 + 2 * i] = half_bits_to_float((uint16_t)(h1[i] & 0xFFFFu));
+    v[8 + 2 * i + 1] = half_bits_to_float((uint16_t)(h1[i] >> 16));
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  const uint16_t s16 = float_to_half_bits(amax / 31.0f);
+  const float sf = half_bits_to_float(s16);
+  int q[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    int c = 0;
+    if (sf != 0.0f) c = (int)rintf(v[i] / sf);
+    q[i] = c > 31 ? 31 : (c < -31 ? -31 : c);
+  }
+  const u32x3 d = pack_unit(q);
+  uint32_t* dst = wp + unit_dword(n, (int64_t)g * kUnitsPerGroup + j, K);
+  dst[0] = d[0];
+  dst[1] = d[1];
+  dst[2] = d[2];
+  if (j == 0) sw[n * G + g] = s16;
+}
+
+// Thread = 8 consecutive activations; 16 threads = one 128-deep group.
+// blockIdx.x = token row, blockIdx.y = chunk of 2048 columns.
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int K,
+                                                        int qmax, int8_t* __restrict__ qa,
+                                                        float* __restrict__ sa) {
+  const int G = K >> 7;
+  const int64_t m = blockIdx.x;
+  const int k0 = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (k0 >= K) return;  // whole groups drop out together (K % 128 == 0)
+  const u32x4 h = *reinterpret_cast<const u32x4*>(x + m * K + k0);
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = half_bits_to_float((uint16_t)(h[i] & 0xFFFFu));
+    v[2 * i + 1] = half_bits_to_float((uint16_t)(h[i] >> 16));
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  amax = fmaxf(amax, __shfl_xor(amax, 8));
+  const float s = amax / (float)qmax;  // +0 when the group is all zero
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int c = 0;
+    if (s != 0.0f) c = (int)rintf(v[i] / s);
+    c = c > qmax ? qmax : (c < -qmax ? -qmax : c);
+    const uint32_t b = (uint32_t)(c & 0xFF);
+    if (i < 4)
+      lo |= b << (8 * i);
+    else
+      hi |= b << (8 * (i - 4));
+  }
+  u32x2 out;
+  out[0] = lo;
+  out[1] = hi;
+  *reinterpret_cast<u32x2*>(qa + m * K + k0) = out;
+  if ((threadIdx.x & 15) == 0) sa[m * G + (k0 >> 7)] = s;
+}
+
+hipError_t launch_pack_w6(const uint16_t* w, int64_t N, int64_t K, uint32_t* wp, uint16_t* sw,
+                          hipStream_t stream) {
+  dim3 grid((unsigned)(N / 16), (unsigned)(K / kGroup));
+  hipLaunchKernelGGL(pack_w6_kernel, grid, dim3(128), 0, stream, w, (int)K, wp, sw);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int qmax, int8_t* qa,
+                            float* sa, hipStream_t stream) {
+  dim3 grid((unsigned)M, (unsigned)((K + 2047) / 2048));
+  hipLaunchKernelGGL(quant_act_kernel, grid, dim3(256), 0, stream, x, (int)K, qmax, qa, sa);
+  return hipGetLastError();
+}
+
+}  // namespace flexq

@@ -1,0 +1,79 @@
+// w6_device.h -- gfx950 device helpers shared by the W6Ax kernels.
+//
+// Weight unit (16 six-bit codes in 3 dwords, 4-bit plane + 2-bit plane as in the
+// ZeroQuant(4+2) split) -> four int8x4 MFMA operand dwords whose bytes are 4*q:
+// the 6-bit field lands in bits 2..7 of each byte and bits 0..1 are zero, so the
+// sign comes for free and an int8 MFMA over these bytes yields exactly 4 * (the
+// group dot of the FlexQ BTC section).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flexq {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 128;          // K-group of the method (BTC section: 128-deep K groups)
+constexpr int kUnitsPerGroup = 8;    // 16 codes per unit
+constexpr int kUnitDwords = 3;
+
+// Decode one unit into 16 int8 lanes holding 4*q, code i in byte i.
+__device__ __forceinline__ i32x4 unpack_unit_x4(uint32_t d0, uint32_t d1, uint32_t d2) {
+  i32x4 e;
+  e[0] = (int32_t)(((d0 << 2) & 0x3C3C3C3Cu) | ((d2 << 6) & 0xC0C0C0C0u));
+  e[1] = (int32_t)(((d0 >> 2) & 0x3C3C3C3Cu) | ((d2 << 4) & 0xC0C0C0C0u));
+  e[2] = (int32_t)(((d1 << 2) & 0x3C3C3C3Cu) | ((d2 << 2) & 0xC0C0C0C0u));
+  e[3] = (int32_t)(((d1 >> 2) & 0x3C3C3C3Cu) | (d2 & 0xC0C0C0C0u));
+  return e;
+}
+
+// Encode 16 codes (q in [-32, 31]) into one unit.
+__device__ __forceinline__ u32x3 pack_unit(const int q[16]) {
+  uint32_t d0 = 0, d1 = 0, d2 = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t v0 = (uint32_t)q[j] & 63u, v1 = (uint32_t)q[4 + j] & 63u;
+    uint32_t v2 = (uint32_t)q[8 + j] & 63u, v3 = (uint32_t)q[12 + j] & 63u;
+    d0 |= ((v0 & 15u) | ((v1 & 15u) << 4)) << (8 * j);
+    d1 |= ((v2 & 15u) | ((v3 & 15u) << 4)) << (8 * j);
+    d2 |= ((v0 >> 4) | ((v1 >> 4) << 2) | ((v2 >> 4) << 4) | ((v3 >> 4) << 6)) << (8 * j);
+  }
+  u32x3 r;
+  r[0] = d0;
+  r[1] = d1;
+  r[2] = d2;
+  return r;
+}
+
+// First dword of unit (n, u = k/16) of an N x K packed weight.
+__host__ __device__ __forceinline__ int64_t unit_dword(int64_t n, int64_t u, int64_t K) {
+  return 3 * (((n >> 4) * (K >> 4) + u) * 16 + (n & 15));
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32, round to nearest even
+}
+
+// 16x16x64 int8 MFMA: lane l supplies A row (l % 16) and B column (l % 16), 16 bytes
+// each, for k-block (l / 16); D lane l holds column l % 16, rows 4*(l/16) .. +3.
+__device__ __forceinline__ i32x4 mfma16(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// 32x32x32 int8 MFMA: lane l supplies A row (l % 32) and B column (l % 32), 16 bytes
+// each, for k-block (l / 32); D lane l holds column l % 32 and, in register r,
+// row 8*(r/4) + 4*(l/32) + r%4.
+__device__ __forceinline__ i32x16 mfma32(i32x4 a, i32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+}  // namespace flexq
