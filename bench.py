@@ -104,7 +104,7 @@ def main():
                                   nthreads=nthreads)
             xd = torch.from_numpy(x).to(dev)
             qa = torch.empty((M, K), dtype=torch.int8, device=dev)
-            sa = torch.empty((M, K // GROUP), dtype=torch.float32, device=dev)
+            sa = torch.empty((K // GROUP, M), dtype=torch.float32, device=dev)
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
             bufs[(M, name)] = (x, xd, qa, sa, y)
     torch.cuda.synchronize()
@@ -237,7 +237,7 @@ def cpu_baseline(bufs, m_list, cols, packed, gpu_ms_per_step, tot_ops):
         wp, sw = packed[name][0]
         n = min(cols, N)
         wps = wp[: n * K * 3 // 16].cpu().numpy().view(np.uint32)  # first n/16 tiles
-        sws = sw[:n].cpu().numpy()
+        sws = np.ascontiguousarray(sw[:, :n].cpu().numpy().T)      # [n][G] for the oracle
         wq[name] = (oracle.unpack_codes(wps, n, K), sws, n)
     for M in m_list:
         for ab in ABITS:

@@ -24,8 +24,9 @@
  *   W   fp16 [N][K]         nn.Linear weight ([out][in]); Y = X * W^T
  *   X   fp16 [M][K]         activations, one row per token
  *   q_a int8 [M][K]         quantized activations (one code per byte)
- *   s_a fp32 [M][K/128]     activation scales
- *   s_w fp16 [N][K/128]     weight scales
+ *   s_a fp32 [K/128][M]     activation scales, group-major: s_a[g][m] at g*M + m
+ *   s_w fp16 [K/128][N]     weight scales, group-major: s_w[g][n] at g*N + n
+ *                           (group-major so one group's scales are contiguous)
  *   w_packed                6-bit weight codes, 16 codes per 3 dwords:
  *       v = q & 63, lo = v & 15, hi = v >> 4 (q in [-31, 31]; -32 decodes but is
  *       never produced), for byte j = 0..3 of each dword:
@@ -95,7 +96,7 @@ size_t flexq_packed_w6_bytes(int64_t N, int64_t K);
    weights; blog, "Fine-Grained Quantization ...": one scale per group).
      w_fp16   [N][K] fp16 bits, 16-byte aligned          (input)
      w_packed flexq_packed_w6_bytes(N, K) bytes, 16-byte aligned (output)
-     s_w_fp16 [N][K/128] fp16 bits, 2-byte aligned        (output)
+     s_w_fp16 [K/128][N] fp16 bits, 2-byte aligned        (output)
    N == 0 is a no-op.  Errors: INVALID_VALUE (null, N < 0, K <= 0, overlap),
    UNSUPPORTED (group_size != 128, K % 128, N % 16, alignment). */
 flexq_status flexq_pack_w6(const uint16_t* w_fp16, int64_t N, int64_t K, int32_t group_size,
@@ -106,7 +107,7 @@ flexq_status flexq_pack_w6(const uint16_t* w_fp16, int64_t N, int64_t K, int32_t
    layers, 8-bit in sensitive ones).
      x_fp16 [M][K] fp16 bits, 16-byte aligned (input)
      q_a    [M][K] int8, 8-byte aligned       (output)
-     s_a    [M][K/128] fp32, 4-byte aligned   (output)
+     s_a    [K/128][M] fp32, 4-byte aligned   (output; M is its row stride)
    M == 0 is a no-op.  Errors as for flexq_pack_w6, plus INVALID_VALUE for abits. */
 flexq_status flexq_quant_act(const uint16_t* x_fp16, int64_t M, int64_t K, int32_t group_size,
                              int32_t abits, int8_t* q_a, float* s_a, void* stream);
@@ -115,8 +116,8 @@ flexq_status flexq_quant_act(const uint16_t* x_fp16, int64_t M, int64_t K, int32
    (blog, "Bridging Software and Hardware with BTC": exact integer group products,
    dequantization fused into the GEMM).  The result is bit-identical to the formula
    in this header's preamble on every path.
-     q_a      [M][K] int8, 16-byte aligned     s_a [M][K/128] fp32, 4-byte aligned
-     w_packed packed codes, 16-byte aligned   s_w [N][K/128] fp16, 2-byte aligned
+     q_a      [M][K] int8, 16-byte aligned     s_a [K/128][M] fp32, 4-byte aligned
+     w_packed packed codes, 16-byte aligned   s_w [K/128][N] fp16, 2-byte aligned
      y_fp16   [M][N] fp16, 4-byte aligned (output)
    abits (6 or 8) is validated; both are stored as int8 so the product is the same.
    M == 0 or N == 0 is a no-op. */

@@ -43,6 +43,11 @@ def u32(t):
     return t.cpu().numpy().view(np.uint32)
 
 
+def gm(a):
+    """Oracle scales [rows][groups] -> the library's group-major [groups][rows]."""
+    return np.ascontiguousarray(np.asarray(a).T)
+
+
 def inputs(seed, M, N, K):
     x = synth.activations(synth.derive_seed(seed, "x", M, N, K), M, K)
     w = synth.weights(synth.derive_seed(seed, "w", M, N, K), N, K)
@@ -61,7 +66,7 @@ def test_pack_w6_bit_exact(fq, N, K):
     wp_ref, sw_ref = oracle.pack_w6(w)
     wp, sw = fq.pack_w6(to_dev(w))
     torch.cuda.synchronize()
-    assert np.array_equal(u16(sw), sw_ref.view(np.uint16))
+    assert np.array_equal(u16(sw), gm(sw_ref).view(np.uint16))
     assert np.array_equal(u32(wp), wp_ref)
 
 
@@ -79,7 +84,7 @@ def test_pack_w6_edge_values(fq):
     w[5, G:2 * G] = -w[4, :G]
     wp_ref, sw_ref = oracle.pack_w6(w)
     wp, sw = fq.pack_w6(to_dev(w))
-    assert np.array_equal(u16(sw), sw_ref.view(np.uint16))
+    assert np.array_equal(u16(sw), gm(sw_ref).view(np.uint16))
     assert np.array_equal(u32(wp), wp_ref)
 
 
@@ -95,7 +100,7 @@ def test_quant_act_bit_exact(fq, M, K, abits):
     qa_ref, sa_ref = oracle.quant_act(x, abits)
     qa, sa = fq.quant_act(to_dev(x), abits)
     torch.cuda.synchronize()
-    assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_ref.view(np.uint32))
+    assert np.array_equal(sa.cpu().numpy().view(np.uint32), gm(sa_ref).view(np.uint32))
     assert np.array_equal(qa.cpu().numpy(), qa_ref)
 
 
@@ -111,7 +116,7 @@ def test_quant_act_edge_values(fq, abits):
     x[4, G:2 * G] = (rng.standard_normal(G) * 1e-7).astype(np.float16)
     qa_ref, sa_ref = oracle.quant_act(x, abits)
     qa, sa = fq.quant_act(to_dev(x), abits)
-    assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_ref.view(np.uint32))
+    assert np.array_equal(sa.cpu().numpy().view(np.uint32), gm(sa_ref).view(np.uint32))
     assert np.array_equal(qa.cpu().numpy(), qa_ref)
 
 
@@ -158,8 +163,8 @@ def run_gemm_case(fq, M, N, K, abits, path, seed=4):
     qa, sa = oracle.quant_act(x, abits)
     wp, sw = oracle.pack_w6(w)
     y_ref = oracle.gemm_packed(qa, sa, wp, sw, N)
-    y = fq.gemm_w6ax(to_dev(qa), to_dev(sa), to_dev(wp.view(np.int32)), to_dev(sw), N, abits,
-                     path=path)
+    y = fq.gemm_w6ax(to_dev(qa), to_dev(gm(sa)), to_dev(wp.view(np.int32)), to_dev(gm(sw)), N,
+                     abits, path=path)
     got = u16(y)
     bad = np.argwhere(got != y_ref.view(np.uint16))
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
@@ -167,7 +172,7 @@ def run_gemm_case(fq, M, N, K, abits, path, seed=4):
 
 SHAPES = [(16, 256, 512), (1, 16, 128), (5, 48, 1152), (17, 272, 640), (33, 160, 384),
           (64, 128, 2048), (65, 144, 512), (128, 256, 1024), (130, 400, 768), (257, 96, 256),
-          (300, 528, 1280)]
+          (300, 528, 1280), (1024, 256, 512), (1100, 400, 384), (2048, 128, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -194,8 +199,8 @@ def test_gemm_zero_rows_and_zero_groups(fq):
         qa, sa = oracle.quant_act(x, 6)
         wp, sw = oracle.pack_w6(w)
         y_ref = oracle.gemm_packed(qa, sa, wp, sw, N)
-        y = fq.gemm_w6ax(to_dev(qa), to_dev(sa), to_dev(wp.view(np.int32)), to_dev(sw), N, 6,
-                         path=path)
+        y = fq.gemm_w6ax(to_dev(qa), to_dev(gm(sa)), to_dev(wp.view(np.int32)), to_dev(gm(sw)), N,
+                         6, path=path)
         assert np.array_equal(u16(y), y_ref.view(np.uint16))
 
 
@@ -206,7 +211,7 @@ def test_gemm_deterministic_and_in_bounds(fq):
     x, w = inputs(10, M, N, K)
     qa, sa = oracle.quant_act(x, 8)
     wp, sw = oracle.pack_w6(w)
-    args = (to_dev(qa), to_dev(sa), to_dev(wp.view(np.int32)), to_dev(sw))
+    args = (to_dev(qa), to_dev(gm(sa)), to_dev(wp.view(np.int32)), to_dev(gm(sw)))
     for path in (1, 2):
         buf = torch.full((M * N + 4096,), -1, dtype=torch.int16, device=DEV)
         y = buf[:M * N].view(torch.float16).view(M, N)
@@ -237,7 +242,8 @@ def test_stream_argument_is_honoured(fq):
     wp, sw = oracle.pack_w6(w)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        d_qa, d_sa, d_wp, d_sw = (to_dev(qa), to_dev(sa), to_dev(wp.view(np.int32)), to_dev(sw))
+        d_qa, d_sa, d_wp, d_sw = (to_dev(qa), to_dev(gm(sa)), to_dev(wp.view(np.int32)),
+                                  to_dev(gm(sw)))
         y = fq.gemm_w6ax(d_qa, d_sa, d_wp, d_sw, N, 6)
     s.synchronize()
     assert np.array_equal(u16(y), oracle.gemm_packed(qa, sa, wp, sw, N).view(np.uint16))

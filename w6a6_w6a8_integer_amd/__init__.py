@@ -100,13 +100,14 @@ def packed_w6_words(N: int, K: int) -> int:
 
 def pack_w6(w: torch.Tensor, w_packed: torch.Tensor | None = None,
             s_w: torch.Tensor | None = None):
-    """fp16 W[N][K] -> (w_packed int32[3*N*K/16] holding the packed dwords, s_w fp16[N][K/128])."""
+    """fp16 W[N][K] -> (w_packed int32[3*N*K/16] holding the packed dwords,
+    s_w fp16[K/128][N], group-major)."""
     _cuda(w, torch.float16, "w")
     N, K = w.shape
     if w_packed is None:
         w_packed = torch.empty(max(1, packed_w6_words(N, K)), dtype=torch.int32, device=w.device)
     if s_w is None:
-        s_w = torch.empty((N, K // GROUP), dtype=torch.float16, device=w.device)
+        s_w = torch.empty((K // GROUP, N), dtype=torch.float16, device=w.device)
     _check(lib().flexq_pack_w6(w.data_ptr(), N, K, GROUP, w_packed.data_ptr(), s_w.data_ptr(),
                                _stream(w)), "flexq_pack_w6")
     return w_packed, s_w
@@ -114,13 +115,13 @@ def pack_w6(w: torch.Tensor, w_packed: torch.Tensor | None = None,
 
 def quant_act(x: torch.Tensor, abits: int, q_a: torch.Tensor | None = None,
               s_a: torch.Tensor | None = None):
-    """fp16 X[M][K] -> (q_a int8[M][K], s_a fp32[M][K/128]); abits 6 or 8."""
+    """fp16 X[M][K] -> (q_a int8[M][K], s_a fp32[K/128][M], group-major); abits 6 or 8."""
     _cuda(x, torch.float16, "x")
     M, K = x.shape
     if q_a is None:
         q_a = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if s_a is None:
-        s_a = torch.empty((M, K // GROUP), dtype=torch.float32, device=x.device)
+        s_a = torch.empty((K // GROUP, M), dtype=torch.float32, device=x.device)
     _check(lib().flexq_quant_act(x.data_ptr(), M, K, GROUP, abits, q_a.data_ptr(),
                                  s_a.data_ptr(), _stream(x)), "flexq_quant_act")
     return q_a, s_a

@@ -43,6 +43,11 @@ inline flexq_status check_n(int64_t N) {
   return FLEXQ_SUCCESS;
 }
 
+// the group-major scale arrays are addressed with 32-bit byte offsets
+inline flexq_status check_scales(int64_t rows, int64_t K) {
+  return rows * (K / kGroup) < (1LL << 29) ? FLEXQ_SUCCESS : FLEXQ_ERROR_UNSUPPORTED;
+}
+
 inline flexq_status check_m(int64_t M) {
   if (M < 0) return FLEXQ_ERROR_INVALID_VALUE;
   if (M > kMaxM) return FLEXQ_ERROR_UNSUPPORTED;
@@ -104,6 +109,7 @@ flexq_status flexq_pack_w6(const uint16_t* w_fp16, int64_t N, int64_t K, int32_t
                            uint32_t* w_packed, uint16_t* s_w_fp16, void* stream) {
   FLEXQ_TRY(check_n(N));
   FLEXQ_TRY(check_k(K, group_size));
+  FLEXQ_TRY(check_scales(N, K));
   if (N == 0) return FLEXQ_SUCCESS;
   if (!w_fp16 || !w_packed || !s_w_fp16) return FLEXQ_ERROR_INVALID_VALUE;
   if (!aligned(w_fp16, 16) || !aligned(w_packed, 16) || !aligned(s_w_fp16, 2))
@@ -119,6 +125,7 @@ flexq_status flexq_quant_act(const uint16_t* x_fp16, int64_t M, int64_t K, int32
                              int32_t abits, int8_t* q_a, float* s_a, void* stream) {
   FLEXQ_TRY(check_m(M));
   FLEXQ_TRY(check_k(K, group_size));
+  FLEXQ_TRY(check_scales(M, K));
   if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
   if (M == 0) return FLEXQ_SUCCESS;
   if (!x_fp16 || !q_a || !s_a) return FLEXQ_ERROR_INVALID_VALUE;
@@ -138,6 +145,8 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a, const uin
   FLEXQ_TRY(check_m(M));
   FLEXQ_TRY(check_n(N));
   FLEXQ_TRY(check_k(K, group_size));
+  FLEXQ_TRY(check_scales(M, K));
+  FLEXQ_TRY(check_scales(N, K));
   if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
   if (path != FLEXQ_PATH_AUTO && path != FLEXQ_PATH_DECODE && path != FLEXQ_PATH_PREFILL)
     return FLEXQ_ERROR_INVALID_VALUE;

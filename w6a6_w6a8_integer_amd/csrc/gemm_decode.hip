@@ -61,8 +61,10 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
   // Out-of-range buffer loads return zero: rows >= `rows` and groups >= G vanish.
   const auto rw = make_rsrc(wp + (size_t)tile * 3 * K, 12u * (uint32_t)K);
   const auto ra = make_rsrc(qa + (size_t)row0 * K, (uint32_t)rows * (uint32_t)K);
-  const auto rsa = make_rsrc(sa + (size_t)row0 * G, (uint32_t)rows * (uint32_t)G * 4u);
-  const auto rsw = make_rsrc(sw + (size_t)tile * 16 * G, 32u * (uint32_t)G);
+  // scales are group-major (s_a[g][m] at g*M + m, s_w[g][n] at g*N + n); entries of
+  // rows past this block are read but never used
+  const auto rsa = make_rsrc(sa + row0, (uint32_t)((size_t)G * M - row0) * 4u);
+  const auto rsw = make_rsrc(sw + (size_t)tile * 16, (uint32_t)((size_t)G * N - tile * 16) * 2u);
 
   __shared__ int32_t lds_d[2][S][OUTS];
   __shared__ float lds_sa[2][S][ROWS];
@@ -81,9 +83,12 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
         b.a[ms][j] = __builtin_amdgcn_raw_buffer_load_b128(
             ra, a_lane_off + (uint32_t)(ms * 16) * (uint32_t)K + g * 128u + j * 64u, 0, 0);
     }
+    // (every offset goes in the VGPR operand: the range check that zeroes reads
+    // past the buffer does not cover the scalar offset)
     b.sa = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rsa, ((uint32_t)lane * G + g) * 4u, 0, 0));
-    b.sw = __builtin_amdgcn_raw_buffer_load_b16(rsw, ((uint32_t)(lane & 15) * G + g) * 2u, 0, 0);
+        float, __builtin_amdgcn_raw_buffer_load_b32(rsa, ((uint32_t)lane + g * (uint32_t)M) * 4u, 0, 0));
+    b.sw = __builtin_amdgcn_raw_buffer_load_b16(rsw, ((uint32_t)(lane & 15) + g * (uint32_t)N) * 2u,
+                                                0, 0);
   };
 
   Bundle<MT> ring[P];

@@ -14,10 +14,9 @@ namespace flexq {
 // One workgroup = one 16-row tile x one 128-deep group.  Thread t handles row
 // t/8 of the tile and unit t%8 of the group (16 codes); the 8 threads of a row
 // are adjacent lanes, so the group max is a 3-step butterfly.
-__global__ __launch_bounds__(128) void pack_w6_kernel(const uint16_t* __restrict__ w, int K,
-                                                      uint32_t* __restrict__ wp,
+__global__ __launch_bounds__(128) void pack_w6_kernel(const uint16_t* __restrict__ w, int N,
+                                                      int K, uint32_t* __restrict__ wp,
                                                       uint16_t* __restrict__ sw) {
-  const int G = K >> 7;
   const int t = threadIdx.x;
   const int r = t >> 3, j = t & 7;
   const int64_t n = (int64_t)blockIdx.x * 16 + r;
@@ -52,15 +51,14 @@ __global__ __launch_bounds__(128) void pack_w6_kernel(const uint16_t* __restrict
   dst[0] = d[0];
   dst[1] = d[1];
   dst[2] = d[2];
-  if (j == 0) sw[n * G + g] = s16;
+  if (j == 0) sw[(int64_t)g * N + n] = s16;  // group-major scales
 }
 
 // Thread = 8 consecutive activations; 16 threads = one 128-deep group.
 // blockIdx.x = token row, blockIdx.y = chunk of 2048 columns.
-__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int K,
-                                                        int qmax, int8_t* __restrict__ qa,
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int M,
+                                                        int K, int qmax, int8_t* __restrict__ qa,
                                                         float* __restrict__ sa) {
-  const int G = K >> 7;
   const int64_t m = blockIdx.x;
   const int k0 = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (k0 >= K) return;  // whole groups drop out together (K % 128 == 0)
@@ -95,20 +93,21 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
   out[0] = lo;
   out[1] = hi;
   *reinterpret_cast<u32x2*>(qa + m * K + k0) = out;
-  if ((threadIdx.x & 15) == 0) sa[m * G + (k0 >> 7)] = s;
+  if ((threadIdx.x & 15) == 0) sa[(int64_t)(k0 >> 7) * M + m] = s;  // group-major scales
 }
 
 hipError_t launch_pack_w6(const uint16_t* w, int64_t N, int64_t K, uint32_t* wp, uint16_t* sw,
                           hipStream_t stream) {
   dim3 grid((unsigned)(N / 16), (unsigned)(K / kGroup));
-  hipLaunchKernelGGL(pack_w6_kernel, grid, dim3(128), 0, stream, w, (int)K, wp, sw);
+  hipLaunchKernelGGL(pack_w6_kernel, grid, dim3(128), 0, stream, w, (int)N, (int)K, wp, sw);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int qmax, int8_t* qa,
                             float* sa, hipStream_t stream) {
   dim3 grid((unsigned)M, (unsigned)((K + 2047) / 2048));
-  hipLaunchKernelGGL(quant_act_kernel, grid, dim3(256), 0, stream, x, (int)K, qmax, qa, sa);
+  hipLaunchKernelGGL(quant_act_kernel, grid, dim3(256), 0, stream, x, (int)M, (int)K, qmax, qa,
+                     sa);
   return hipGetLastError();
 }
 

@@ -59,8 +59,13 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// binary32 -> binary16, round to nearest even, of an already rounded binary32 value.
+// The empty asm hides where `f` came from: hipcc 7.2 otherwise folds a final
+// fmaf + conversion into one v_fma_mix (a single rounding straight to fp16), which
+// differs from rounding to fp32 first whenever the fp32 result is an fp16 tie.
 __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
-  return __builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32, round to nearest even
+  asm volatile("" : "+v"(f));
+  return __builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32
 }
 
 // 16x16x64 int8 MFMA: lane l supplies A row (l % 16) and B column (l % 16), 16 bytes
