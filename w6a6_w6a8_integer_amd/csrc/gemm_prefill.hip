@@ -169,15 +169,15 @@ __global__ __launch_bounds__(BM * 2, 512 / (BM * 2)) void gemm_prefill_kernel(
     u32x3 u[C::B_UNITS];
     uint32_t s;
   };
-  BRegs breg;
+  BRegs breg[2];  // group h lives in set h % 2 from its issue until its fill
 
   // Register half of group g's reads: packed weights and weight scales.
-  auto issue_regs = [&](int g) {
+  auto issue_regs = [&](int g, BRegs& r) {
     const uint32_t bo = b_voff + (uint32_t)g * 1536u;
 #pragma unroll
     for (int i = 0; i < C::B_UNITS; ++i)
-      breg.u[i] = __builtin_amdgcn_raw_buffer_load_b96(rw, bo + 12u * i, 0, 0);
-    breg.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u, 0, 0);
+      r.u[i] = __builtin_amdgcn_raw_buffer_load_b96(rw, bo + 12u * i, 0, 0);
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u, 0, 0);
   };
   // DMA half of group g's reads: activations and activation scales into stage s.
   auto issue_dma = [&](int g, int s) {
@@ -190,17 +190,17 @@ __global__ __launch_bounds__(BM * 2, 512 / (BM * 2)) void gemm_prefill_kernel(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(stage_sa(s) + sa_row0), 4,
                                              sa_voff + (uint32_t)g * (uint32_t)M * 4u, 0, 0, 0);
   };
-  // Unpack the register half into stage s.
-  auto fill = [&](int s) {
+  // Unpack a register set into stage s.
+  auto fill = [&](int s, const BRegs& r) {
     int8_t* lb = stage_b(s);
 #pragma unroll
     for (int i = 0; i < C::B_UNITS; ++i)
       *reinterpret_cast<i32x4*>(lb + b_lds0 + 16 * i) =
-          unpack_unit_x4(breg.u[i][0], breg.u[i][1], breg.u[i][2]);
-    stage_s4(s)[sw_col] = 0.25f * half_bits_to_float((uint16_t)breg.s);  // exact
+          unpack_unit_x4(r.u[i][0], r.u[i][1], r.u[i][2]);
+    stage_s4(s)[sw_col] = 0.25f * half_bits_to_float((uint16_t)r.s);  // exact
   };
-  // Wait until everything but this wave's newest DMA batch has landed.
-  auto wait_all_but_dma = [&]() { wait_vm_lgkm0<C::DMA_OPS>(); };
+  // vector-memory instructions issued per group: register loads + DMA
+  constexpr int OPS_PER_GROUP = C::B_UNITS + 1 + C::DMA_OPS;
 
   float acc[2][2][16];
 #pragma unroll
@@ -249,24 +249,27 @@ __global__ __launch_bounds__(BM * 2, 512 / (BM * 2)) void gemm_prefill_kernel(
     }
   };
 
-  // ---- prologue: group 0 staged, group 1's DMA in flight.  Past the last group
-  // (here and in the loop) the last group is simply read again into stages that
-  // are never read, so the loop body has no branches and no read leaves the buffers.
+  // ---- prologue: group 0 staged, group 1 in flight.  Past the last group (here
+  // and in the loop) the last group is simply read again into stages that are
+  // never read, so the loop body has no branches and no read leaves the buffers.
   const int glast = G - 1;
-  issue_regs(0);
+  issue_regs(0, breg[0]);
   issue_dma(0, 0);
+  issue_regs(min(1, glast), breg[1]);
   issue_dma(min(1, glast), 1);
-  wait_all_but_dma();
-  fill(0);
+  wait_vm_lgkm0<OPS_PER_GROUP>();  // group 0 landed
+  fill(0, breg[0]);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   barrier();
 
   const int frag = lane * 16;
-  for (int g = 0; g < G; ++g) {
+  // One group.  `mine` held group g (unpacked during the previous group) and now
+  // receives group g+2; `other` holds group g+1, unpacked here.
+  auto step = [&](int g, BRegs& mine, const BRegs& other) __attribute__((always_inline)) {
     const int s = g % STAGES;
-    // registers for g+1 first, then the DMA for g+2: the wait at the end of this
-    // group can then leave the DMA in flight (loads complete in issue order)
-    issue_regs(min(g + 1, glast));
+    // group g+2: registers, and DMA into the stage group g-1 used; both stay in
+    // flight across this group's barrier
+    issue_regs(min(g + 2, glast), mine);
     issue_dma(min(g + 2, glast), (g + 2) % STAGES);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -318,6 +321,9 @@ __global__ __launch_bounds__(BM * 2, 512 / (BM * 2)) void gemm_prefill_kernel(
       }
     }
     rescale(acc[0], d0, sa0, s4c);
+    fill((g + 1) % STAGES, other);  // group g+1, loaded during the previous group
+#pragma unroll
+    for (int r = 0; r < 16; ++r) saprev[r] = lsa[rowoff0 + 32 + 8 * (r >> 2) + (r & 3)];
     anchor(acc[0]);
     anchor(d1);
 #pragma unroll
@@ -331,16 +337,22 @@ __global__ __launch_bounds__(BM * 2, 512 / (BM * 2)) void gemm_prefill_kernel(
     // the second half is rescaled during the next group's first half
     dprev[0] = d1[0];
     dprev[1] = d1[1];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) saprev[r] = lsa[rowoff0 + 32 + 8 * (r >> 2) + (r & 3)];
     s4prev[0] = s4c[0];
     s4prev[1] = s4c[1];
 
-    wait_all_but_dma();  // group g+1's registers and DMA have landed
-    fill((g + 1) % STAGES);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fills and reads of this group done
+    // everything issued before this group's loads has landed (group g+1's DMA), and
+    // this group's fills and LDS reads are done before anyone passes the barrier
+    wait_vm_lgkm0<OPS_PER_GROUP>();
     barrier();
+  };
+  // Unrolled by two so each register set is named statically; no branch sits
+  // between a load and the unpack that consumes it.
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    step(g, breg[0], breg[1]);
+    step(g + 1, breg[1], breg[0]);
   }
+  if (g < G) step(g, breg[0], breg[1]);
   wait_vm_lgkm0<0>();  // no copy into LDS may outlive the workgroup
   rescale(acc[1], dprev, saprev, s4prev);
 
