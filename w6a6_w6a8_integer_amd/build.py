@@ -18,8 +18,11 @@ ARCH = "gfx950"
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
-    # packed fp32 VALU ops stay off; the host pass warns and ignores it
+    # no packed fp32 VALU ops in generated code; the host pass warns and ignores it
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the fused dequant reads every one with the VALU,
+    # and results parked in AGPRs would cost a copy each
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     # the quantizers and the fused dequant need exact IEEE binary32
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-mcode-object-version=5",

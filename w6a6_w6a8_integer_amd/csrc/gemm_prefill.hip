@@ -34,6 +34,8 @@
 // Workgroups are numbered so that the 8 XCDs each take a contiguous run of
 // logical tiles (hardware hands workgroup i to XCD i % 8), and logical tiles run
 // over a band of GM row blocks before moving to the next column block.
+#include <utility>
+
 #include "kernels.h"
 #include "w6_device.h"
 
@@ -65,6 +67,38 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// acc += S' * t, where S' is lane R of the caller's 16-lane row of S (DPP
+// row_newbcast on the first source; S is only ever written by LDS loads, so no
+// VALU-to-DPP wait states are needed).
+template <int R>
+__device__ __forceinline__ void fmac_row_bcast(float& acc, float S, float t) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc)
+      : "v"(S), "v"(t), "i"(R));
+}
+
+// Rescale outputs R0 .. R0+3 of one 32x32 tile: t = RN(d * s_w) from the biased
+// MFMA result F = 12582912 + 4d, then acc = RN(t * s_a + acc).  The s_a of output r
+// sits in lane r of each 16-lane row of the packed register S.
+template <int R0>
+__device__ __forceinline__ void rescale4(float (&a)[16], const f32x16& F, float s4, float bias,
+                                         float S) {
+  const float t0 = fmaf(F[R0 + 0], s4, bias);
+  const float t1 = fmaf(F[R0 + 1], s4, bias);
+  const float t2 = fmaf(F[R0 + 2], s4, bias);
+  const float t3 = fmaf(F[R0 + 3], s4, bias);
+  fmac_row_bcast<R0 + 0>(a[R0 + 0], S, t0);
+  fmac_row_bcast<R0 + 1>(a[R0 + 1], S, t1);
+  fmac_row_bcast<R0 + 2>(a[R0 + 2], S, t2);
+  fmac_row_bcast<R0 + 3>(a[R0 + 3], S, t3);
+}
+
+// f(integral_constant<int, K>) for K = 0 .. n-1, in order.
+template <class F, int... K>
+__device__ __forceinline__ void unroll(F&& f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+
 }  // namespace
 
 template <int BM>
@@ -84,12 +118,13 @@ struct PrefillCfg {
 };
 
 template <int BM>
-__global__ __launch_bounds__(BM * 2, 512 / (BM * 2)) void gemm_prefill_kernel(
+__global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint32_t* __restrict__ wp,
     const uint16_t* __restrict__ sw, int M, int N, int K, int GM, uint16_t* __restrict__ y) {
   using C = PrefillCfg<BM>;
   static_assert(C::A_BLOCKS_PER_WAVE == 4, "tile/thread mismatch");
   static_assert(C::B_UNITS * C::THREADS == BN * 8, "B split");
+  static_assert(C::B_UNITS == 2 || C::B_UNITS == 4, "unpack schedule covers 2 or 4 units");
 
   const int G = K >> 7;
   const int tid = threadIdx.x;
@@ -113,14 +148,6 @@ __global__ __launch_bounds__(BM * 2, 512 / (BM * 2)) void gemm_prefill_kernel(
   const int ncols = min(BN, N - n0);
 
   __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * C::STAGE_BYTES];
-  auto stage_a = [&](int s) { return lds + s * C::STAGE_BYTES; };
-  auto stage_b = [&](int s) { return lds + s * C::STAGE_BYTES + C::A_BYTES; };
-  auto stage_sa = [&](int s) {
-    return reinterpret_cast<float*>(lds + s * C::STAGE_BYTES + C::A_BYTES + C::B_BYTES);
-  };
-  auto stage_s4 = [&](int s) {
-    return reinterpret_cast<float*>(lds + s * C::STAGE_BYTES + C::A_BYTES + C::B_BYTES + BM * 4);
-  };
 
   // Out-of-range loads return zero: rows >= M and columns >= N vanish.
   const auto ra = make_rsrc(qa + (size_t)m0 * K, (uint32_t)mrows * (uint32_t)K);
@@ -179,25 +206,32 @@ __global__ __launch_bounds__(BM * 2, 512 / (BM * 2)) void gemm_prefill_kernel(
       r.u[i] = __builtin_amdgcn_raw_buffer_load_b96(rw, bo + 12u * i, 0, 0);
     r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u, 0, 0);
   };
-  // DMA half of group g's reads: activations and activation scales into stage s.
-  auto issue_dma = [&](int g, int s) {
-    int8_t* la = stage_a(s);
+  // DMA half of group g's reads: activations and activation scales into the stage
+  // at byte offset `so`.
+  auto issue_dma = [&](int g, int so) {
+    int8_t* la = lds + so;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (lds_ptr_t)(la + (wave * 4 + i) * 1024), 16,
           ((i & 1) ? a_voff1 : a_voff0) + (uint32_t)g * 128u + (uint32_t)(i * 8) * K, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(stage_sa(s) + sa_row0), 4,
-                                             sa_voff + (uint32_t)g * (uint32_t)M * 4u, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsa, (lds_ptr_t)(la + C::A_BYTES + C::B_BYTES + sa_row0 * 4), 4,
+        sa_voff + (uint32_t)g * (uint32_t)M * 4u, 0, 0, 0);
   };
-  // Unpack a register set into stage s.
-  auto fill = [&](int s, const BRegs& r) {
-    int8_t* lb = stage_b(s);
+  // Unpack unit i of a register set, and its weight scale, into the stage at `so`.
+  auto fill_unit = [&](int so, const BRegs& r, int i) {
+    *reinterpret_cast<i32x4*>(lds + so + C::A_BYTES + b_lds0 + 16 * i) =
+        unpack_unit_x4(r.u[i][0], r.u[i][1], r.u[i][2]);
+  };
+  auto fill_scale = [&](int so, const BRegs& r) {
+    *reinterpret_cast<float*>(lds + so + C::A_BYTES + C::B_BYTES + BM * 4 + sw_col * 4) =
+        0.25f * half_bits_to_float((uint16_t)r.s);  // exact
+  };
+  auto fill = [&](int so, const BRegs& r) {
 #pragma unroll
-    for (int i = 0; i < C::B_UNITS; ++i)
-      *reinterpret_cast<i32x4*>(lb + b_lds0 + 16 * i) =
-          unpack_unit_x4(r.u[i][0], r.u[i][1], r.u[i][2]);
-    stage_s4(s)[sw_col] = 0.25f * half_bits_to_float((uint16_t)r.s);  // exact
+    for (int i = 0; i < C::B_UNITS; ++i) fill_unit(so, r, i);
+    fill_scale(so, r);
   };
   // vector-memory instructions issued per group: register loads + DMA
   constexpr int OPS_PER_GROUP = C::B_UNITS + 1 + C::DMA_OPS;
@@ -214,39 +248,38 @@ __global__ __launch_bounds__(BM * 2, 512 / (BM * 2)) void gemm_prefill_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) magic[r] = (int32_t)kMagic;
 
-  // deferred second half of the previous group: MFMA results + its scales; starting
-  // values make the first deferred rescale add exactly 0 (t = fma(F0, 0, 0) = 0)
+  // Deferred row tile 1 of the previous group: MFMA results, its packed s_a
+  // register and s_w / 4.  The starting values make the first deferred rescale add
+  // exactly +0 (t = fma(F0, 0, -0) = +0, then acc + S * t with S = 0).
   i32x16 dprev[2] = {magic, magic};
-  float saprev[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) saprev[r] = 0.0f;
+  float Sprev = 0.0f;
   float s4prev[2] = {0.0f, 0.0f};
 
-  auto rescale = [&](float (&a)[2][16], const i32x16 (&d)[2], const float (&sav)[16],
-                     const float (&s4v)[2]) {
+  // per-lane byte offsets inside a stage
+  const int r32 = lane & 31, hl = lane >> 5;
+  int a_off[4];  // A fragment of k-chunk c, row tile 0 (row tile 1: +4096)
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) {
-      const float bias = -kMagicF * s4v[tn];
-      // reinterpret the whole vector: with hipcc 7.2 a bit_cast of one subscripted
-      // vector element silently reads element 0
-      const f32x16 Fv = __builtin_bit_cast(f32x16, d[tn]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) a[tn][r] = fmaf(fmaf(Fv[r], s4v[tn], bias), sav[r], a[tn][r]);
-    }
-  };
+  for (int c = 0; c < 4; ++c)
+    a_off[c] = (wm * 64 + r32) * 128 + (((2 * c + hl) ^ ((r32 >> 1) & 7)) * 16);
+  // B fragment (c, tn): block c * (BN / 32) + wn * 2 + tn, lane-linear
+  const int b_off = C::A_BYTES + wn * 2048 + lane * 16;
+  // s_a row held by this lane in the packed scale register of row tile tm (+128 * tm)
+  const int sa_off =
+      C::A_BYTES + C::B_BYTES + (wm * 64 + 8 * ((lane >> 2) & 3) + 4 * hl + (lane & 3)) * 4;
+  // s_w / 4 of this lane's column in column tile tn (+128 * tn)
+  const int s4_off = C::A_BYTES + C::B_BYTES + BM * 4 + (wn * 64 + r32) * 4;
 
-  // Pin values to this point of the instruction stream (keeps each rescale inside
-  // the MFMA phase it is meant to overlap instead of being sunk to the loop end).
-  auto anchor = [](auto& v) {
-    if constexpr (sizeof(v) == 2 * 16 * sizeof(float)) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(v[t][r]));
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) asm volatile("" : "+v"(v[t]));
-    }
+  auto ldA = [&](int so, int c, int tm) {
+    return *reinterpret_cast<const i32x4*>(lds + so + a_off[c] + tm * 4096);
+  };
+  auto ldB = [&](int so, int c, int tn) {
+    return *reinterpret_cast<const i32x4*>(lds + so + b_off + c * 4096 + tn * 1024);
+  };
+  auto ldS = [&](int so, int tm) {
+    return *reinterpret_cast<const float*>(lds + so + sa_off + tm * 128);
+  };
+  auto ldS4 = [&](int so, int tn) {
+    return *reinterpret_cast<const float*>(lds + so + s4_off + tn * 128);
   };
 
   // ---- prologue: group 0 staged, group 1 in flight.  Past the last group (here
@@ -256,87 +289,97 @@ __global__ __launch_bounds__(BM * 2, 512 / (BM * 2)) void gemm_prefill_kernel(
   issue_regs(0, breg[0]);
   issue_dma(0, 0);
   issue_regs(min(1, glast), breg[1]);
-  issue_dma(min(1, glast), 1);
+  issue_dma(min(1, glast), C::STAGE_BYTES);
   wait_vm_lgkm0<OPS_PER_GROUP>();  // group 0 landed
   fill(0, breg[0]);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   barrier();
 
-  const int frag = lane * 16;
-  // One group.  `mine` held group g (unpacked during the previous group) and now
-  // receives group g+2; `other` holds group g+1, unpacked here.
-  auto step = [&](int g, BRegs& mine, const BRegs& other) __attribute__((always_inline)) {
-    const int s = g % STAGES;
-    // group g+2: registers, and DMA into the stage group g-1 used; both stay in
-    // flight across this group's barrier
+  // One group g in stage `so`, written as 16 steps of one MFMA each.  The first
+  // eight (row tile 0) overlap the rescale of the previous group's row tile 1, the
+  // last eight (row tile 1) the rescale of this group's row tile 0 and the unpack
+  // of group g+1.  LDS reads run two or more steps ahead of their MFMA; the B
+  // fragments stay in registers for both row tiles.  `mine` held group g and now
+  // receives group g+2; `other` holds group g+1.
+  auto step_group = [&](int g, int so, int so_next, int so_dma, BRegs& mine,
+                        const BRegs& other) __attribute__((always_inline)) {
     issue_regs(min(g + 2, glast), mine);
-    issue_dma(min(g + 2, glast), (g + 2) % STAGES);
+    issue_dma(min(g + 2, glast), so_dma);
+
+    i32x4 a0[4], a1[4], b[4][2];
+    i32x16 d0[2], d1[2];
+    float S0, S1, s4c[2];
+    const f32x16 Fp0 = __builtin_bit_cast(f32x16, dprev[0]);
+    const f32x16 Fp1 = __builtin_bit_cast(f32x16, dprev[1]);
+    const float bp0 = -kMagicF * s4prev[0], bp1 = -kMagicF * s4prev[1];
+    const float Sp = Sprev;
+
+    a0[0] = ldA(so, 0, 0);
+    b[0][0] = ldB(so, 0, 0);
+    b[0][1] = ldB(so, 0, 1);
+    a0[1] = ldA(so, 1, 0);
+    b[1][0] = ldB(so, 1, 0);
+    b[1][1] = ldB(so, 1, 1);
+    rescale4<0>(acc[1][0], Fp0, s4prev[0], bp0, Sp);
     __builtin_amdgcn_sched_barrier(0);
 
-    const int8_t* la = stage_a(s);
-    const int8_t* lb = stage_b(s);
-    const float* lsa = stage_sa(s);
-    const float* ls4 = stage_s4(s);
-    const int rowoff0 = wm * 64 + 4 * (lane >> 5);
-
-    // phase 1: MFMAs of row tile 0 (both column tiles) while the VALU rescales the
-    // previous group's row tile 1; also fetch this group's scales for phase 2
-    i32x16 d0[2];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const i32x4 af = *reinterpret_cast<const i32x4*>(la + a_frag[c]);
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn) {
-        const i32x4 bf =
-            *reinterpret_cast<const i32x4*>(lb + (c * (BN / 32) + wn * 2 + tn) * 1024 + frag);
-        d0[tn] = mfma32(af, bf, c == 0 ? magic : d0[tn]);
+    // ---- row tile 0
+    unroll([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int c = k >> 1, tn = k & 1;
+      if constexpr (k == 0) a0[2] = ldA(so, 2, 0);
+      if constexpr (k == 1) b[2][0] = ldB(so, 2, 0);
+      if constexpr (k == 2) b[2][1] = ldB(so, 2, 1);
+      if constexpr (k == 3) a0[3] = ldA(so, 3, 0);
+      if constexpr (k == 4) b[3][0] = ldB(so, 3, 0);
+      if constexpr (k == 5) b[3][1] = ldB(so, 3, 1);
+      if constexpr (k == 6) {
+        a1[0] = ldA(so, 0, 1);
+        S0 = ldS(so, 0);
+        s4c[0] = ldS4(so, 0);
+        s4c[1] = ldS4(so, 1);
       }
-    }
-    rescale(acc[1], dprev, saprev, s4prev);
-    anchor(acc[1]);
-    anchor(d0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // eight VALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // phase 2: MFMAs of row tile 1 while the VALU rescales row tile 0 of this group
-    float sa0[16], s4c[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sa0[r] = lsa[rowoff0 + 8 * (r >> 2) + (r & 3)];
-#pragma unroll
-    for (int tn = 0; tn < 2; ++tn) s4c[tn] = ls4[wn * 64 + tn * 32 + (lane & 31)];
-    i32x16 d1[2];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const i32x4 af = *reinterpret_cast<const i32x4*>(la + a_frag[c] + 32 * 128);
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn) {
-        const i32x4 bf =
-            *reinterpret_cast<const i32x4*>(lb + (c * (BN / 32) + wn * 2 + tn) * 1024 + frag);
-        d1[tn] = mfma32(af, bf, c == 0 ? magic : d1[tn]);
+      if constexpr (k == 7) {
+        a1[1] = ldA(so, 1, 1);
+        S1 = ldS(so, 1);
       }
-    }
-    rescale(acc[0], d0, sa0, s4c);
-    fill((g + 1) % STAGES, other);  // group g+1, loaded during the previous group
-#pragma unroll
-    for (int r = 0; r < 16; ++r) saprev[r] = lsa[rowoff0 + 32 + 8 * (r >> 2) + (r & 3)];
-    anchor(acc[0]);
-    anchor(d1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      d0[tn] = mfma32(a0[c], b[c][tn], c == 0 ? magic : d0[tn]);
+      // outputs 4 .. 31 of the deferred tile, four per step
+      if constexpr (k < 7) {
+        constexpr int o = 4 * (k + 1);
+        if constexpr (o < 16)
+          rescale4<o>(acc[1][0], Fp0, s4prev[0], bp0, Sp);
+        else
+          rescale4<o - 16>(acc[1][1], Fp1, s4prev[1], bp1, Sp);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }, std::make_integer_sequence<int, 8>{});
 
-    // the second half is rescaled during the next group's first half
+    // ---- row tile 1
+    const f32x16 F00 = __builtin_bit_cast(f32x16, d0[0]);
+    const f32x16 F01 = __builtin_bit_cast(f32x16, d0[1]);
+    unroll([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int c = k >> 1, tn = k & 1;
+      if constexpr (k == 0) a1[2] = ldA(so, 2, 1);
+      if constexpr (k == 1) a1[3] = ldA(so, 3, 1);
+      d1[tn] = mfma32(a1[c], b[c][tn], c == 0 ? magic : d1[tn]);
+      if constexpr (k < 4)
+        rescale4<4 * k>(acc[0][0], F00, s4c[0], -kMagicF * s4c[0], S0);
+      else
+        rescale4<4 * (k - 4)>(acc[0][1], F01, s4c[1], -kMagicF * s4c[1], S0);
+      // the unpack of group g+1: its units spread over steps, then its scale
+      constexpr int per = C::B_UNITS <= 2 ? 2 : 1;
+      if constexpr (k >= per && k % per == 0 && k / per - 1 < C::B_UNITS)
+        fill_unit(so_next, other, k / per - 1);
+      if constexpr (k == 6) fill_scale(so_next, other);
+      __builtin_amdgcn_sched_barrier(0);
+    }, std::make_integer_sequence<int, 8>{});
+
+    // row tile 1 is rescaled during the next group's row tile 0
     dprev[0] = d1[0];
     dprev[1] = d1[1];
+    Sprev = S1;
     s4prev[0] = s4c[0];
     s4prev[1] = s4c[1];
 
@@ -345,16 +388,36 @@ __global__ __launch_bounds__(BM * 2, 512 / (BM * 2)) void gemm_prefill_kernel(
     wait_vm_lgkm0<OPS_PER_GROUP>();
     barrier();
   };
+
   // Unrolled by two so each register set is named statically; no branch sits
-  // between a load and the unpack that consumes it.
+  // between a load and the unpack that consumes it.  Stage offsets rotate through
+  // the three stages.
+  int so = 0, so1 = C::STAGE_BYTES, so2 = 2 * C::STAGE_BYTES;
+  auto rotate = [&]() {
+    const int t = so;
+    so = so1;
+    so1 = so2;
+    so2 = t;
+  };
   int g = 0;
   for (; g + 1 < G; g += 2) {
-    step(g, breg[0], breg[1]);
-    step(g + 1, breg[1], breg[0]);
+    step_group(g, so, so1, so2, breg[0], breg[1]);
+    rotate();
+    step_group(g + 1, so, so1, so2, breg[1], breg[0]);
+    rotate();
   }
-  if (g < G) step(g, breg[0], breg[1]);
+  if (g < G) step_group(g, so, so1, so2, breg[0], breg[1]);
   wait_vm_lgkm0<0>();  // no copy into LDS may outlive the workgroup
-  rescale(acc[1], dprev, saprev, s4prev);
+  {
+    const f32x16 Fp0 = __builtin_bit_cast(f32x16, dprev[0]);
+    const f32x16 Fp1 = __builtin_bit_cast(f32x16, dprev[1]);
+    const float bp0 = -kMagicF * s4prev[0], bp1 = -kMagicF * s4prev[1];
+    unroll([&](auto kc) {
+      constexpr int q = decltype(kc)::value;
+      rescale4<4 * q>(acc[1][0], Fp0, s4prev[0], bp0, Sprev);
+      rescale4<4 * q>(acc[1][1], Fp1, s4prev[1], bp1, Sprev);
+    }, std::make_integer_sequence<int, 4>{});
+  }
 
   // epilogue: fp16 stores, column = lane % 32
 #pragma unroll
