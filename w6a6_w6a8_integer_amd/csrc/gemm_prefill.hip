@@ -233,8 +233,31 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     for (int i = 0; i < C::B_UNITS; ++i) fill_unit(so, r, i);
     fill_scale(so, r);
   };
-  // vector-memory instructions issued per group: register loads + DMA
+  // vector-memory instructions issued per group: DMA + register loads
   constexpr int OPS_PER_GROUP = C::B_UNITS + 1 + C::DMA_OPS;
+  // Vector-memory instruction i of group g (DMA blocks, the s_a row, weight units,
+  // the weight scale), so a group's reads can be spread over the MFMA steps: issued
+  // in one burst by every wave right after a barrier, they queue at the texture unit
+  // and stall the waves behind them.
+  auto vmem_op = [&](auto ic, int g, int so, BRegs& r) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i < 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (lds_ptr_t)(lds + so + (wave * 4 + i) * 1024), 16,
+          ((i & 1) ? a_voff1 : a_voff0) + (uint32_t)g * 128u + (uint32_t)(i * 8) * K, 0, 0, 0);
+    } else if constexpr (i == 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsa, (lds_ptr_t)(lds + so + C::A_BYTES + C::B_BYTES + sa_row0 * 4), 4,
+          sa_voff + (uint32_t)g * (uint32_t)M * 4u, 0, 0, 0);
+    } else if constexpr (i < 5 + C::B_UNITS) {
+      r.u[i - 5] = __builtin_amdgcn_raw_buffer_load_b96(
+          rw, b_voff + (uint32_t)g * 1536u + 12u * (i - 5), 0, 0);
+    } else {
+      r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u,
+                                                 0, 0);
+    }
+  };
+  static_assert(C::DMA_OPS == 5, "vmem_op numbering");
 
   float acc[2][2][16];
 #pragma unroll
@@ -303,8 +326,9 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // receives group g+2; `other` holds group g+1.
   auto step_group = [&](int g, int so, int so_next, int so_dma, BRegs& mine,
                         const BRegs& other) __attribute__((always_inline)) {
-    issue_regs(min(g + 2, glast), mine);
-    issue_dma(min(g + 2, glast), so_dma);
+    // group g+2 goes to registers `mine` (unpacked last group) and to the stage
+    // group g-1 used, one vector-memory instruction per MFMA step
+    const int gn = min(g + 2, glast);
 
     i32x4 a0[4], a1[4], b[4][2];
     i32x16 d0[2], d1[2];
@@ -327,6 +351,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     unroll([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       constexpr int c = k >> 1, tn = k & 1;
+      vmem_op(kc, gn, so_dma, mine);
       if constexpr (k == 0) a0[2] = ldA(so, 2, 0);
       if constexpr (k == 1) b[2][0] = ldB(so, 2, 0);
       if constexpr (k == 2) b[2][1] = ldB(so, 2, 1);
@@ -361,6 +386,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     unroll([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       constexpr int c = k >> 1, tn = k & 1;
+      if constexpr (8 + k < OPS_PER_GROUP) vmem_op(std::integral_constant<int, 8 + k>{}, gn, so_dma, mine);
       if constexpr (k == 0) a1[2] = ldA(so, 2, 1);
       if constexpr (k == 1) a1[3] = ldA(so, 3, 1);
       d1[tn] = mfma32(a1[c], b[c][tn], c == 0 ? magic : d1[tn]);
