@@ -175,20 +175,25 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // duplicate write is harmless and every wave runs the same instruction stream)
   const int sa_row0 = (wave % C::SA_WAVES) * 64;
   const uint32_t sa_voff = (uint32_t)(sa_row0 + lane) * 4u;
-  // B: thread t owns B_UNITS consecutive unit slots (u_local*16 + n%16) of one
-  // 16-column tile of the group; they share u_local, so their fragment slots are
-  // 16 bytes apart.
-  constexpr int THREADS_PER_TILE = C::THREADS / (BN / 16);
-  const int b_tile = tid / THREADS_PER_TILE;
-  const int b_us0 = (tid % THREADS_PER_TILE) * C::B_UNITS;
-  const uint32_t b_voff = (uint32_t)b_tile * 12u * (uint32_t)K + (uint32_t)b_us0 * 12u;
+  // B: wave w loads the 16-column tiles TPW*w .. TPW*w + TPW - 1 of the group
+  // (1536 contiguous bytes per tile and group, unit slot j = u_local*16 + n%16).
+  // Load i of a lane takes slot (i%2)*64 + lane of tile TPW*w + i/2, so every load
+  // instruction reads 768 contiguous bytes; in fragment order that unit lands at
+  // b_lds0 + (i%2)*8192 + (i/2)*256.
+  constexpr int TPW = (BN / 16) / C::WAVES;
+  static_assert(C::B_UNITS == 2 * TPW && (TPW == 1 || TPW == 2), "B load split");
+  const int b_tile0 = wave * TPW;
+  const uint32_t b_voff = (uint32_t)b_tile0 * 12u * (uint32_t)K + (uint32_t)lane * 12u;
+  auto b_unit_off = [&](int i) -> uint32_t {
+    return (uint32_t)(i >> 1) * 12u * (uint32_t)K + (uint32_t)(i & 1) * 768u;
+  };
   // s_w: thread t handles column t % 128 (duplicates write identical values)
   const int sw_col = tid % BN;
   const uint32_t sw_voff = (uint32_t)sw_col * 2u;
   int b_lds0;
   {
-    const int ul = b_us0 >> 4;
-    const int n = b_tile * 16 + (b_us0 & 15);
+    const int ul = lane >> 4;
+    const int n = b_tile0 * 16 + (lane & 15);
     b_lds0 = (((ul >> 1) * (BN / 32) + (n >> 5)) * 64 + (n & 31) + 32 * (ul & 1)) * 16;
   }
 
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     const uint32_t bo = b_voff + (uint32_t)g * 1536u;
 #pragma unroll
     for (int i = 0; i < C::B_UNITS; ++i)
-      r.u[i] = __builtin_amdgcn_raw_buffer_load_b96(rw, bo + 12u * i, 0, 0);
+      r.u[i] = __builtin_amdgcn_raw_buffer_load_b96(rw, bo + b_unit_off(i), 0, 0);
     r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u, 0, 0);
   };
   // DMA half of group g's reads: activations and activation scales into the stage
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   };
   // Unpack unit i of a register set, and its weight scale, into the stage at `so`.
   auto fill_unit = [&](int so, const BRegs& r, int i) {
-    *reinterpret_cast<i32x4*>(lds + so + C::A_BYTES + b_lds0 + 16 * i) =
+    *reinterpret_cast<i32x4*>(lds + so + C::A_BYTES + b_lds0 + (i & 1) * 8192 + (i >> 1) * 256) =
         unpack_unit_x4(r.u[i][0], r.u[i][1], r.u[i][2]);
   };
   auto fill_scale = [&](int so, const BRegs& r) {
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
           sa_voff + (uint32_t)g * (uint32_t)M * 4u, 0, 0, 0);
     } else if constexpr (i < 5 + C::B_UNITS) {
       r.u[i - 5] = __builtin_amdgcn_raw_buffer_load_b96(
-          rw, b_voff + (uint32_t)g * 1536u + 12u * (i - 5), 0, 0);
+          rw, b_voff + (uint32_t)g * 1536u + b_unit_off(i - 5), 0, 0);
     } else {
       r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u,
                                                  0, 0);
