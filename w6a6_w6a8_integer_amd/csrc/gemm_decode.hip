@@ -7,14 +7,18 @@
 // int8 MFMA (v_mfma_i32_16x16x64_i8) over weights unpacked in registers, and
 // the time goes to streaming the 0.75 B/weight packed matrix from HBM.
 //
-// Work split: one workgroup per 16-column tile of W, S waves.  Round r hands
-// group g = r*S + w to wave w, so a round reads S*1536 contiguous bytes of the
-// tile.  Every wave keeps P rounds of loads in flight (weights, activations and
-// both scales, issued together so the in-order vmcnt never waits on a younger
-// load).  After its two MFMAs a wave parks the 16 x rows int32 dots and the
-// group's scales in LDS; after one barrier the block folds the S groups into
-// the fp32 accumulators in ascending group order, so the result equals the
-// sequential definition bit for bit.
+// Work items are (16-column tile, pass of up to 64 token rows).  The grid is
+// persistent: every workgroup owns a contiguous run of items (so of packed weight
+// memory) and streams through it without a break, its load ring running on from
+// one item into the next.  Inside an item, round r hands group g = r*S + w to
+// wave w, so a round reads S*1536 contiguous bytes of the tile.  Every wave keeps
+// P rounds of loads in flight (weights, activations and both scales, issued
+// together so the in-order vmcnt never waits on a younger load); the weight loads
+// are non-temporal since each weight byte is read exactly once.  After its two
+// MFMAs a wave parks the 16 x rows int32 dots and the group's scales in LDS; after
+// one barrier the block folds the S groups into the fp32 accumulators in
+// ascending group order, so the result equals the sequential definition bit for
+// bit.  The last round of an item stores its fp16 outputs.
 #include "kernels.h"
 #include "w6_device.h"
 
@@ -23,6 +27,7 @@ namespace flexq {
 namespace {
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw 32-bit dword buffer, gfx9 style
+constexpr int kNonTemporal = 2;                // cache-policy bit of buffer loads
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
@@ -37,12 +42,29 @@ struct Bundle {
   uint32_t sw;      // s_w[col = lane%16][g] (fp16 bits)
 };
 
+// Position of a round in a workgroup's stream: item (= pass * ntiles + tile) and
+// round r within it, advanced one round at a time.
+struct Cursor {
+  int item, tile, pass, r;
+  __device__ __forceinline__ void next(int R, int ntiles) {
+    if (++r == R) {
+      r = 0;
+      ++item;
+      if (++tile == ntiles) {
+        tile = 0;
+        ++pass;
+      }
+    }
+  }
+};
+
 }  // namespace
 
 template <int MT, int S, int P>
 __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint32_t* __restrict__ wp,
-    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ y) {
+    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ y, int ntiles,
+    int items, int per_wg) {
   static_assert(P % 2 == 0, "slot parity must be static");
   constexpr int ROWS = MT * 16;
   constexpr int OUTS = ROWS * 16;
@@ -52,19 +74,11 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
   const int G = K >> 7;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int tile = blockIdx.x;
-  const int row0 = blockIdx.y * 64;
-  const int rows = min(ROWS, M - row0);  // >= 1
-  const int R = (G + S - 1) / S;
-  const int Rp = (R + P - 1) / P * P;
-
-  // Out-of-range buffer loads return zero: rows >= `rows` and groups >= G vanish.
-  const auto rw = make_rsrc(wp + (size_t)tile * 3 * K, 12u * (uint32_t)K);
-  const auto ra = make_rsrc(qa + (size_t)row0 * K, (uint32_t)rows * (uint32_t)K);
-  // scales are group-major (s_a[g][m] at g*M + m, s_w[g][n] at g*N + n); entries of
-  // rows past this block are read but never used
-  const auto rsa = make_rsrc(sa + row0, (uint32_t)((size_t)G * M - row0) * 4u);
-  const auto rsw = make_rsrc(sw + (size_t)tile * 16, (uint32_t)((size_t)G * N - tile * 16) * 2u);
+  const int R = (G + S - 1) / S;  // rounds per item
+  const int item_begin = blockIdx.x * per_wg;
+  const int item_end = min(items, item_begin + per_wg);
+  const int Q = (item_end - item_begin) * R;  // rounds of this workgroup (> 0)
+  const int Qp = (Q + P - 1) / P * P;
 
   __shared__ int32_t lds_d[2][S][OUTS];
   __shared__ float lds_sa[2][S][ROWS];
@@ -72,10 +86,25 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
 
   const uint32_t a_lane_off = (uint32_t)(lane & 15) * (uint32_t)K + (uint32_t)(lane >> 4) * 16u;
 
-  auto load = [&](Bundle<MT>& b, int r) {
-    const uint32_t g = (uint32_t)(r * S + wave);
-    b.w[0] = __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + lane) * 12u, 0, 0);
-    b.w[1] = __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + 64u + lane) * 12u, 0, 0);
+  // Loads of round (c.item, c.r).  Out-of-range buffer loads return zero: rows past
+  // the pass and groups >= G vanish; rounds past this workgroup's last item read
+  // from empty buffers.
+  auto load = [&](Bundle<MT>& b, const Cursor& c) {
+    const bool live = c.item < item_end;
+    const int tile = live ? c.tile : 0;
+    const int row0 = live ? c.pass * 64 : 0;
+    const int rows = live ? min(ROWS, M - row0) : 0;
+    const auto rw = make_rsrc(wp + (size_t)tile * 3 * K, live ? 12u * (uint32_t)K : 0u);
+    const auto ra = make_rsrc(qa + (size_t)row0 * K, (uint32_t)rows * (uint32_t)K);
+    // scales are group-major (s_a[g][m] at g*M + m, s_w[g][n] at g*N + n); entries of
+    // rows past the pass are read but never used
+    const auto rsa = make_rsrc(sa + row0, live ? (uint32_t)((size_t)G * M - row0) * 4u : 0u);
+    const auto rsw = make_rsrc(sw + (size_t)tile * 16,
+                               live ? (uint32_t)((size_t)G * N - tile * 16) * 2u : 0u);
+    const uint32_t g = (uint32_t)(c.r * S + wave);
+    b.w[0] = __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + lane) * 12u, 0, kNonTemporal);
+    b.w[1] =
+        __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + 64u + lane) * 12u, 0, kNonTemporal);
 #pragma unroll
     for (int ms = 0; ms < MT; ++ms) {
 #pragma unroll
@@ -91,19 +120,25 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
                                                 0, 0);
   };
 
+  const Cursor start{item_begin, item_begin % ntiles, item_begin / ntiles, 0};
+  Cursor cl = start;  // next round to load
   Bundle<MT> ring[P];
 #pragma unroll
-  for (int p = 0; p < P; ++p) load(ring[p], p);
+  for (int p = 0; p < P; ++p) {
+    load(ring[p], cl);
+    cl.next(R, ntiles);
+  }
 
   float acc[OPT];
 #pragma unroll
   for (int i = 0; i < OPT; ++i) acc[i] = 0.0f;
 
+  Cursor cp = start;  // round being processed
   const i32x4 zero = {0, 0, 0, 0};
-  for (int r0 = 0; r0 < Rp; r0 += P) {
+  for (int q0 = 0; q0 < Qp; q0 += P) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int r = r0 + p;
+      const int q = q0 + p;
       const int slot = p & 1;
       Bundle<MT>& b = ring[p];
       // exact integer group products (4*d, see w6_device.h)
@@ -123,41 +158,88 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
           lds_d[slot][wave][(ms * 16 + 4 * (lane >> 4) + i) * 16 + (lane & 15)] = d[ms][i];
       if (lane < ROWS) lds_sa[slot][wave][lane] = b.sa;
       if (lane < 16) lds_sw[slot][wave][lane] = half_bits_to_float((uint16_t)b.sw);
-      load(b, r + P);
+      load(b, cl);
+      cl.next(R, ntiles);
       __syncthreads();
-      // fold the S groups of this round, ascending g
-      const int gbase = r * S;
-      const int ng = min(S, G - gbase);
+      if (q < Q) {  // workgroup-uniform
+        // fold the S groups of this round, ascending g
+        const int row0 = cp.pass * 64;
+        const int rows = min(ROWS, M - row0);
+        const int ng = min(S, G - cp.r * S);
 #pragma unroll
-      for (int i = 0; i < OPT; ++i) {
-        const int o = threadIdx.x + i * THREADS;
-        if (o < OUTS && (o >> 4) < rows) {
-          const int row = o >> 4, col = o & 15;
-          float a = acc[i];
-          for (int w = 0; w < ng; ++w) {
-            const float t = (float)(lds_d[slot][w][o] >> 2) * lds_sw[slot][w][col];
-            a = fmaf(t, lds_sa[slot][w][row], a);
+        for (int i = 0; i < OPT; ++i) {
+          const int o = threadIdx.x + i * THREADS;
+          if (o < OUTS && (o >> 4) < rows) {
+            const int row = o >> 4, col = o & 15;
+            // all reads first, then the dependent chain
+            int dv[S];
+            float swv[S], sav[S];
+#pragma unroll
+            for (int w = 0; w < S; ++w) {
+              dv[w] = lds_d[slot][w][o];
+              swv[w] = lds_sw[slot][w][col];
+              sav[w] = lds_sa[slot][w][row];
+            }
+            float a = acc[i];
+#pragma unroll
+            for (int w = 0; w < S; ++w) {
+              if (w < ng) {
+                const float t = (float)(dv[w] >> 2) * swv[w];
+                a = fmaf(t, sav[w], a);
+              }
+            }
+            acc[i] = a;
           }
-          acc[i] = a;
         }
+        if (cp.r == R - 1) {  // item complete: store and restart the accumulators
+          const int tile = cp.tile;
+#pragma unroll
+          for (int i = 0; i < OPT; ++i) {
+            const int o = threadIdx.x + i * THREADS;
+            if (o < OUTS && (o >> 4) < rows)
+              y[(size_t)(row0 + (o >> 4)) * N + (size_t)tile * 16 + (o & 15)] =
+                  float_to_half_bits(acc[i]);
+            acc[i] = 0.0f;
+          }
+        }
+        cp.next(R, ntiles);
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < OPT; ++i) {
-    const int o = threadIdx.x + i * THREADS;
-    if (o < OUTS && (o >> 4) < rows)
-      y[(size_t)(row0 + (o >> 4)) * N + (size_t)tile * 16 + (o & 15)] = float_to_half_bits(acc[i]);
-  }
 }
+
+namespace {
+
+int cu_count() {
+  static int cached[64];  // per device; 0 = not yet queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace
 
 template <int MT, int S, int P>
 static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint32_t* wp,
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                   uint16_t* y, hipStream_t stream) {
-  dim3 grid((unsigned)(N / 16), (unsigned)((M + 63) / 64));
-  hipLaunchKernelGGL((gemm_decode_kernel<MT, S, P>), grid, dim3(64 * S), 0, stream, qa, sa, wp,
-                     sw, (int)M, (int)N, (int)K, y);
+  const int64_t ntiles = N / 16;
+  const int64_t items = ntiles * ((M + 63) / 64);
+  if (items > INT32_MAX) return hipErrorInvalidValue;  // item indices are 32-bit
+  // one resident workgroup per CU; each takes an equal contiguous share of items
+  const int64_t grid0 = std::min<int64_t>(items, cu_count());
+  const int64_t per_wg = (items + grid0 - 1) / grid0;
+  const int64_t grid = (items + per_wg - 1) / per_wg;
+  hipLaunchKernelGGL((gemm_decode_kernel<MT, S, P>), dim3((unsigned)grid), dim3(64 * S), 0,
+                     stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, y, (int)ntiles, (int)items,
+                     (int)per_wg);
   return hipGetLastError();
 }
 
