@@ -170,9 +170,12 @@ def run_gemm_case(fq, M, N, K, abits, path, seed=4):
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
 
 
+# (the two wide shapes make the decode kernel pair adjacent column tiles, with a
+# half-empty last pair)
 SHAPES = [(16, 256, 512), (1, 16, 128), (5, 48, 1152), (17, 272, 640), (33, 160, 384),
           (64, 128, 2048), (65, 144, 512), (128, 256, 1024), (130, 400, 768), (257, 96, 256),
-          (300, 528, 1280), (1024, 256, 512), (1100, 400, 384), (2048, 128, 1024)]
+          (300, 528, 1280), (1024, 256, 512), (1100, 400, 384), (2048, 128, 1024),
+          (7, 16368, 256), (20, 16368, 384)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

@@ -7,7 +7,9 @@
 // int8 MFMA (v_mfma_i32_16x16x64_i8) over weights unpacked in registers, and
 // the time goes to streaming the 0.75 B/weight packed matrix from HBM.
 //
-// Work items are (16-column tile, pass of up to 64 token rows).  The grid is
+// Work items are (T adjacent 16-column tiles, pass of up to 64 token rows); a wave
+// unpacks the weights of all T tiles of its group against one set of activation
+// fragments, so activations are fetched once per T tiles.  The grid is
 // persistent: every workgroup owns a contiguous run of items (so of packed weight
 // memory) and streams through it without a break, its load ring running on from
 // one item into the next.  Inside an item, round r hands group g = r*S + w to
@@ -34,16 +36,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                            kRsrcWord3);
 }
 
-template <int MT>
+template <int MT, int T>
 struct Bundle {
-  u32x3 w[2];       // two weight units (k-blocks of 64)
+  u32x3 w[T][2];    // per 16-column tile: two weight units (k-blocks of 64)
   i32x4 a[MT][2];   // activation fragments, rows ms*16 + lane%16
   float sa;         // s_a[row = lane][g]
-  uint32_t sw;      // s_w[col = lane%16][g] (fp16 bits)
+  uint32_t sw;      // s_w[col = lane % (16*T)][g] (fp16 bits)
 };
 
-// Position of a round in a workgroup's stream: item (= pass * ntiles + tile) and
-// round r within it, advanced one round at a time.
+// Position of a round in a workgroup's stream: item (= pass * ntiles + tile, a
+// tile being T adjacent 16-column tiles here) and round r within it, advanced one
+// round at a time.
 struct Cursor {
   int item, tile, pass, r;
   __device__ __forceinline__ void next(int R, int ntiles) {
@@ -60,14 +63,15 @@ struct Cursor {
 
 }  // namespace
 
-template <int MT, int S, int P>
+template <int MT, int T, int S, int P>
 __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint32_t* __restrict__ wp,
-    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ y, int ntiles,
-    int items, int per_wg) {
+    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ y, int ntiles16,
+    int ntiles, int items, int per_wg) {
   static_assert(P % 2 == 0, "slot parity must be static");
   constexpr int ROWS = MT * 16;
-  constexpr int OUTS = ROWS * 16;
+  constexpr int COLS = T * 16;
+  constexpr int OUTS = ROWS * COLS;
   constexpr int THREADS = 64 * S;
   constexpr int OPT = (OUTS + THREADS - 1) / THREADS;
 
@@ -82,29 +86,35 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
 
   __shared__ int32_t lds_d[2][S][OUTS];
   __shared__ float lds_sa[2][S][ROWS];
-  __shared__ float lds_sw[2][S][16];
+  __shared__ float lds_sw[2][S][COLS];
 
   const uint32_t a_lane_off = (uint32_t)(lane & 15) * (uint32_t)K + (uint32_t)(lane >> 4) * 16u;
 
   // Loads of round (c.item, c.r).  Out-of-range buffer loads return zero: rows past
   // the pass and groups >= G vanish; rounds past this workgroup's last item read
   // from empty buffers.
-  auto load = [&](Bundle<MT>& b, const Cursor& c) {
+  auto load = [&](Bundle<MT, T>& b, const Cursor& c) {
     const bool live = c.item < item_end;
-    const int tile = live ? c.tile : 0;
+    const int tile = live ? c.tile : 0;  // in units of COLS columns
     const int row0 = live ? c.pass * 64 : 0;
     const int rows = live ? min(ROWS, M - row0) : 0;
-    const auto rw = make_rsrc(wp + (size_t)tile * 3 * K, live ? 12u * (uint32_t)K : 0u);
     const auto ra = make_rsrc(qa + (size_t)row0 * K, (uint32_t)rows * (uint32_t)K);
     // scales are group-major (s_a[g][m] at g*M + m, s_w[g][n] at g*N + n); entries of
-    // rows past the pass are read but never used
+    // rows past the pass or columns past N are read but never used
     const auto rsa = make_rsrc(sa + row0, live ? (uint32_t)((size_t)G * M - row0) * 4u : 0u);
-    const auto rsw = make_rsrc(sw + (size_t)tile * 16,
-                               live ? (uint32_t)((size_t)G * N - tile * 16) * 2u : 0u);
+    const auto rsw = make_rsrc(sw + (size_t)tile * COLS,
+                               live ? (uint32_t)((size_t)G * N - tile * COLS) * 2u : 0u);
     const uint32_t g = (uint32_t)(c.r * S + wave);
-    b.w[0] = __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + lane) * 12u, 0, kNonTemporal);
-    b.w[1] =
-        __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + 64u + lane) * 12u, 0, kNonTemporal);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int t16 = tile * T + t;
+      const bool in = live && t16 < ntiles16;
+      const auto rw = make_rsrc(wp + (size_t)(in ? t16 : 0) * 3 * K, in ? 12u * (uint32_t)K : 0u);
+      b.w[t][0] =
+          __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + lane) * 12u, 0, kNonTemporal);
+      b.w[t][1] =
+          __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + 64u + lane) * 12u, 0, kNonTemporal);
+    }
 #pragma unroll
     for (int ms = 0; ms < MT; ++ms) {
 #pragma unroll
@@ -116,13 +126,13 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
     // past the buffer does not cover the scalar offset)
     b.sa = __builtin_bit_cast(
         float, __builtin_amdgcn_raw_buffer_load_b32(rsa, ((uint32_t)lane + g * (uint32_t)M) * 4u, 0, 0));
-    b.sw = __builtin_amdgcn_raw_buffer_load_b16(rsw, ((uint32_t)(lane & 15) + g * (uint32_t)N) * 2u,
-                                                0, 0);
+    b.sw = __builtin_amdgcn_raw_buffer_load_b16(
+        rsw, ((uint32_t)(lane % COLS) + g * (uint32_t)N) * 2u, 0, 0);
   };
 
   const Cursor start{item_begin, item_begin % ntiles, item_begin / ntiles, 0};
   Cursor cl = start;  // next round to load
-  Bundle<MT> ring[P];
+  Bundle<MT, T> ring[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     load(ring[p], cl);
@@ -140,24 +150,30 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
     for (int p = 0; p < P; ++p) {
       const int q = q0 + p;
       const int slot = p & 1;
-      Bundle<MT>& b = ring[p];
+      Bundle<MT, T>& b = ring[p];
       // exact integer group products (4*d, see w6_device.h)
-      const i32x4 b0 = unpack_unit_x4(b.w[0][0], b.w[0][1], b.w[0][2]);
-      const i32x4 b1 = unpack_unit_x4(b.w[1][0], b.w[1][1], b.w[1][2]);
-      i32x4 d[MT];
+      i32x4 d[T][MT];
 #pragma unroll
-      for (int ms = 0; ms < MT; ++ms) {
-        d[ms] = mfma16(b.a[ms][0], b0, zero);
-        d[ms] = mfma16(b.a[ms][1], b1, d[ms]);
+      for (int t = 0; t < T; ++t) {
+        const i32x4 b0 = unpack_unit_x4(b.w[t][0][0], b.w[t][0][1], b.w[t][0][2]);
+        const i32x4 b1 = unpack_unit_x4(b.w[t][1][0], b.w[t][1][1], b.w[t][1][2]);
+#pragma unroll
+        for (int ms = 0; ms < MT; ++ms) {
+          d[t][ms] = mfma16(b.a[ms][0], b0, zero);
+          d[t][ms] = mfma16(b.a[ms][1], b1, d[t][ms]);
+        }
       }
       // park dots (row-major [row][col]) and this group's scales
 #pragma unroll
-      for (int ms = 0; ms < MT; ++ms)
+      for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          lds_d[slot][wave][(ms * 16 + 4 * (lane >> 4) + i) * 16 + (lane & 15)] = d[ms][i];
+        for (int ms = 0; ms < MT; ++ms)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            lds_d[slot][wave][(ms * 16 + 4 * (lane >> 4) + i) * COLS + t * 16 + (lane & 15)] =
+                d[t][ms][i];
       if (lane < ROWS) lds_sa[slot][wave][lane] = b.sa;
-      if (lane < 16) lds_sw[slot][wave][lane] = half_bits_to_float((uint16_t)b.sw);
+      if (lane < COLS) lds_sw[slot][wave][lane] = half_bits_to_float((uint16_t)b.sw);
       load(b, cl);
       cl.next(R, ntiles);
       __syncthreads();
@@ -169,8 +185,8 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
 #pragma unroll
         for (int i = 0; i < OPT; ++i) {
           const int o = threadIdx.x + i * THREADS;
-          if (o < OUTS && (o >> 4) < rows) {
-            const int row = o >> 4, col = o & 15;
+          if (o < OUTS && o / COLS < rows) {
+            const int row = o / COLS, col = o % COLS;
             // all reads first, then the dependent chain
             int dv[S];
             float swv[S], sav[S];
@@ -196,9 +212,9 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
 #pragma unroll
           for (int i = 0; i < OPT; ++i) {
             const int o = threadIdx.x + i * THREADS;
-            if (o < OUTS && (o >> 4) < rows)
-              y[(size_t)(row0 + (o >> 4)) * N + (size_t)tile * 16 + (o & 15)] =
-                  float_to_half_bits(acc[i]);
+            const int n = tile * COLS + o % COLS;
+            if (o < OUTS && o / COLS < rows && n < N)
+              y[(size_t)(row0 + o / COLS) * N + n] = float_to_half_bits(acc[i]);
             acc[i] = 0.0f;
           }
         }
@@ -226,20 +242,21 @@ int cu_count() {
 
 }  // namespace
 
-template <int MT, int S, int P>
+template <int MT, int T, int S, int P>
 static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint32_t* wp,
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                   uint16_t* y, hipStream_t stream) {
-  const int64_t ntiles = N / 16;
+  const int64_t ntiles16 = N / 16;
+  const int64_t ntiles = (ntiles16 + T - 1) / T;
   const int64_t items = ntiles * ((M + 63) / 64);
   if (items > INT32_MAX) return hipErrorInvalidValue;  // item indices are 32-bit
   // one resident workgroup per CU; each takes an equal contiguous share of items
   const int64_t grid0 = std::min<int64_t>(items, cu_count());
   const int64_t per_wg = (items + grid0 - 1) / grid0;
   const int64_t grid = (items + per_wg - 1) / per_wg;
-  hipLaunchKernelGGL((gemm_decode_kernel<MT, S, P>), dim3((unsigned)grid), dim3(64 * S), 0,
-                     stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, y, (int)ntiles, (int)items,
-                     (int)per_wg);
+  hipLaunchKernelGGL((gemm_decode_kernel<MT, T, S, P>), dim3((unsigned)grid), dim3(64 * S), 0,
+                     stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, y, (int)ntiles16,
+                     (int)ntiles, (int)items, (int)per_wg);
   return hipGetLastError();
 }
 
@@ -248,10 +265,10 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
                               hipStream_t stream) {
   // rows per pass: 16 * MT; more passes over W only when M > 64
   const int64_t rows = M > 64 ? 64 : M;
-  if (rows <= 16) return launch_decode_t<1, 8, 8>(qa, sa, wp, sw, M, N, K, y, stream);
-  if (rows <= 32) return launch_decode_t<2, 8, 6>(qa, sa, wp, sw, M, N, K, y, stream);
-  if (rows <= 48) return launch_decode_t<3, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
-  return launch_decode_t<4, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 16) return launch_decode_t<1, 2, 8, 6>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 32) return launch_decode_t<2, 2, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 48) return launch_decode_t<3, 1, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
+  return launch_decode_t<4, 1, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
 }
 
 }  // namespace flexq
