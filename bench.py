@@ -34,7 +34,7 @@ GROUP = 128
 LAYERS = synth.LLAMA2_70B
 M_LIST = (1, 16, 64, 256, 1024, 4096)
 ABITS = (6, 8)
-DECODE_MAX_M = 64
+DECODE_MAX_M = 32
 
 
 def gemm_bytes(M, N, K):
@@ -55,10 +55,40 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--seed", type=int, default=synth.BASE_SEED)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-cols", type=int, default=128,
+    p.add_argument("--cpu-sample-cols", type=int, default=512,
                    help="output columns per GEMM in the oracle's timed sample")
     p.add_argument("--m", type=str, default=None, help="comma list overriding the token counts")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="first run one device-to-device copy of this many MiB (the known-size "
+                        "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_prefill_llama2_70b.md")
+PREFILL_SRC = os.path.join(ROOT, "w6a6_w6a8_integer_amd", "csrc", "gemm_prefill.hip")
+
+
+def recorded_traffic():
+    """HBM bytes per prefill launch measured with rocprofv3 counters (FETCH_SIZE +
+    WRITE_SIZE, scaled by a copy kernel of known size), as recorded next to the hash
+    of the kernel source it was taken on; None once that source has changed."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+        src = hashlib.sha256(open(PREFILL_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    rec = {}
+    for line in text.splitlines():
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            rec[k.strip()] = v.strip().strip("`")
+    if rec.get("source_sha256") != src:
+        return None
+    try:
+        return int(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -77,6 +107,15 @@ def main():
 
     fq.lib()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read, {n} bytes written")
+        del src, dst
     m_list = tuple(int(v) for v in args.m.split(",")) if args.m else M_LIST
     nthreads = synth.default_threads()
 
@@ -186,11 +225,14 @@ def main():
     value = tot_ops / (ms_per_step * 1e-3) / 1e12
 
     pre_tops = pre_ops / (pre_ms * 1e-3) / 1e12 if pre_ms else 0.0
+    pre_launches = sum(1 for (M, _, _) in plan if M > DECODE_MAX_M)
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9 if dec_ms else 0.0
     if pre_ms >= dec_ms:
+        # integer ops: the unit is TOP/s against the dense int8 MFMA peak
         roofline = {"kernel": "gemm_prefill_kernel", "bound": "mfma", "achieved": round(pre_tops, 1),
-                    "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(pre_tops / INT8_PEAK_TOPS, 4),
-                    "traffic": None}
+                    "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": round(pre_tops / INT8_PEAK_TOPS, 4),
+                    "traffic": recorded_traffic(), "launches_per_step": pre_launches,
+                    "ops_per_launch": round(pre_ops / len(step_ms) / max(pre_launches, 1))}
     else:
         roofline = {"kernel": "gemm_decode_kernel", "bound": "hbm", "achieved": round(dec_gbs, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
