@@ -265,8 +265,8 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
                               hipStream_t stream) {
   // rows per pass: 16 * MT; more passes over W only when M > 64
   const int64_t rows = M > 64 ? 64 : M;
-  if (rows <= 16) return launch_decode_t<1, 2, 8, 6>(qa, sa, wp, sw, M, N, K, y, stream);
-  if (rows <= 32) return launch_decode_t<2, 2, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 16) return launch_decode_t<1, 2, 16, 2>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 32) return launch_decode_t<2, 2, 16, 2>(qa, sa, wp, sw, M, N, K, y, stream);
   if (rows <= 48) return launch_decode_t<3, 1, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
   return launch_decode_t<4, 1, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
 }
