@@ -44,31 +44,46 @@ struct Bundle {
   uint32_t sw;      // s_w[col = lane % (16*T)][g] (fp16 bits)
 };
 
-// Position of a round in a workgroup's stream: item (= pass * ntiles + tile, a
-// tile being T adjacent 16-column tiles here) and round r within it, advanced one
-// round at a time.
+// Position of a step in a workgroup's stream.  The workgroup's items are cut into
+// chunks of up to C consecutive items of one pass; a chunk runs round-major (round
+// r of all its items, then round r+1), so the activation fragments of a round are
+// fetched once per chunk.  A step is (chunk, round r, item i of the chunk); i runs
+// over all C slots, slots past the chunk's end are empty steps.
 struct Cursor {
-  int item, tile, pass, r;
-  __device__ __forceinline__ void next(int R, int ntiles) {
-    if (++r == R) {
-      r = 0;
-      ++item;
-      if (++tile == ntiles) {
-        tile = 0;
-        ++pass;
+  int chunk_begin, chunk_n, tile0, pass, r, i;
+  __device__ __forceinline__ void start_chunk(int C, int item_end, int ntiles) {
+    chunk_n = min(C, min(item_end - chunk_begin, ntiles - tile0));
+  }
+  __device__ __forceinline__ void next(int C, int R, int item_end, int ntiles) {
+    if (++i == C) {
+      i = 0;
+      if (++r == R) {
+        r = 0;
+        chunk_begin += chunk_n;
+        tile0 += chunk_n;
+        if (tile0 == ntiles) {
+          tile0 = 0;
+          ++pass;
+        }
+        start_chunk(C, item_end, ntiles);
       }
     }
+  }
+  __device__ __forceinline__ bool live(int item_end) const {
+    return chunk_begin < item_end && i < chunk_n;
   }
 };
 
 }  // namespace
 
-template <int MT, int T, int S, int P>
+template <int MT, int T, int S, int P, int C>
 __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint32_t* __restrict__ wp,
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ y, int ntiles16,
     int ntiles, int items, int per_wg) {
   static_assert(P % 2 == 0, "slot parity must be static");
+  constexpr int U = C > P ? C : P;  // steps per loop iteration: ring slot and item static
+  static_assert(U % P == 0 && U % C == 0, "step unroll");
   constexpr int ROWS = MT * 16;
   constexpr int COLS = T * 16;
   constexpr int OUTS = ROWS * COLS;
@@ -81,8 +96,6 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
   const int R = (G + S - 1) / S;  // rounds per item
   const int item_begin = blockIdx.x * per_wg;
   const int item_end = min(items, item_begin + per_wg);
-  const int Q = (item_end - item_begin) * R;  // rounds of this workgroup (> 0)
-  const int Qp = (Q + P - 1) / P * P;
 
   __shared__ int32_t lds_d[2][S][OUTS];
   __shared__ float lds_sa[2][S][ROWS];
@@ -90,12 +103,12 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
 
   const uint32_t a_lane_off = (uint32_t)(lane & 15) * (uint32_t)K + (uint32_t)(lane >> 4) * 16u;
 
-  // Loads of round (c.item, c.r).  Out-of-range buffer loads return zero: rows past
-  // the pass and groups >= G vanish; rounds past this workgroup's last item read
-  // from empty buffers.
-  auto load = [&](Bundle<MT, T>& b, const Cursor& c) {
-    const bool live = c.item < item_end;
-    const int tile = live ? c.tile : 0;  // in units of COLS columns
+  // Loads of step c.  Out-of-range buffer loads return zero: rows past the pass and
+  // groups >= G vanish; empty steps read from empty buffers.  The activation
+  // fragments are loaded by the chunk's first item slot only.
+  auto load = [&](Bundle<MT, T>& b, const Cursor& c, auto first_slot) {
+    const bool live = c.live(item_end);
+    const int tile = live ? c.tile0 + c.i : 0;  // in units of COLS columns
     const int row0 = live ? c.pass * 64 : 0;
     const int rows = live ? min(ROWS, M - row0) : 0;
     const auto ra = make_rsrc(qa + (size_t)row0 * K, (uint32_t)rows * (uint32_t)K);
@@ -115,12 +128,14 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
       b.w[t][1] =
           __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + 64u + lane) * 12u, 0, kNonTemporal);
     }
+    if constexpr (decltype(first_slot)::value) {
 #pragma unroll
-    for (int ms = 0; ms < MT; ++ms) {
+      for (int ms = 0; ms < MT; ++ms) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b.a[ms][j] = __builtin_amdgcn_raw_buffer_load_b128(
-            ra, a_lane_off + (uint32_t)(ms * 16) * (uint32_t)K + g * 128u + j * 64u, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          b.a[ms][j] = __builtin_amdgcn_raw_buffer_load_b128(
+              ra, a_lane_off + (uint32_t)(ms * 16) * (uint32_t)K + g * 128u + j * 64u, 0, 0);
+      }
     }
     // (every offset goes in the VGPR operand: the range check that zeroes reads
     // past the buffer does not cover the scalar offset)
@@ -130,27 +145,38 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
         rsw, ((uint32_t)(lane % COLS) + g * (uint32_t)N) * 2u, 0, 0);
   };
 
-  const Cursor start{item_begin, item_begin % ntiles, item_begin / ntiles, 0};
-  Cursor cl = start;  // next round to load
+  Cursor start{item_begin, 0, item_begin % ntiles, item_begin / ntiles, 0, 0};
+  start.start_chunk(C, item_end, ntiles);
+  Cursor cl = start;  // next step to load; step k goes to ring slot k % P
   Bundle<MT, T> ring[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    load(ring[p], cl);
-    cl.next(R, ntiles);
-  }
+  unroll([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    load(ring[p], cl, std::integral_constant<bool, p % C == 0>{});
+    cl.next(C, R, item_end, ntiles);
+  }, std::make_integer_sequence<int, P>{});
 
-  float acc[OPT];
+  float acc[C][OPT];
 #pragma unroll
-  for (int i = 0; i < OPT; ++i) acc[i] = 0.0f;
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int i = 0; i < OPT; ++i) acc[c][i] = 0.0f;
+  i32x4 a_cur[MT][2];  // activation fragments of the current round
 
-  Cursor cp = start;  // round being processed
+  Cursor cp = start;  // step being processed
   const i32x4 zero = {0, 0, 0, 0};
-  for (int q0 = 0; q0 < Qp; q0 += P) {
+  while (cp.chunk_begin < item_end) {  // workgroup-uniform
+    unroll([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      constexpr int slot = p & 1;
+      constexpr int ci = p % C;  // item slot of this step
+      Bundle<MT, T>& b = ring[p % P];
+      if constexpr (ci == 0) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int q = q0 + p;
-      const int slot = p & 1;
-      Bundle<MT, T>& b = ring[p];
+        for (int ms = 0; ms < MT; ++ms) {
+          a_cur[ms][0] = b.a[ms][0];
+          a_cur[ms][1] = b.a[ms][1];
+        }
+      }
       // exact integer group products (4*d, see w6_device.h)
       i32x4 d[T][MT];
 #pragma unroll
@@ -159,8 +185,8 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
         const i32x4 b1 = unpack_unit_x4(b.w[t][1][0], b.w[t][1][1], b.w[t][1][2]);
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms) {
-          d[t][ms] = mfma16(b.a[ms][0], b0, zero);
-          d[t][ms] = mfma16(b.a[ms][1], b1, d[t][ms]);
+          d[t][ms] = mfma16(a_cur[ms][0], b0, zero);
+          d[t][ms] = mfma16(a_cur[ms][1], b1, d[t][ms]);
         }
       }
       // park dots (row-major [row][col]) and this group's scales
@@ -174,11 +200,13 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
                 d[t][ms][i];
       if (lane < ROWS) lds_sa[slot][wave][lane] = b.sa;
       if (lane < COLS) lds_sw[slot][wave][lane] = half_bits_to_float((uint16_t)b.sw);
-      load(b, cl);
-      cl.next(R, ntiles);
+      // the step P ahead lands in this ring slot; it is the chunk's first item slot
+      // exactly when this one is (P is a multiple of C, or C of P)
+      load(b, cl, std::integral_constant<bool, ((p + P) % C) == 0>{});
+      cl.next(C, R, item_end, ntiles);
       __syncthreads();
-      if (q < Q) {  // workgroup-uniform
-        // fold the S groups of this round, ascending g
+      if (cp.live(item_end)) {  // workgroup-uniform
+        // fold the S groups of this round into item ci's accumulators, ascending g
         const int row0 = cp.pass * 64;
         const int rows = min(ROWS, M - row0);
         const int ng = min(S, G - cp.r * S);
@@ -196,7 +224,7 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
               swv[w] = lds_sw[slot][w][col];
               sav[w] = lds_sa[slot][w][row];
             }
-            float a = acc[i];
+            float a = acc[ci][i];
 #pragma unroll
             for (int w = 0; w < S; ++w) {
               if (w < ng) {
@@ -204,23 +232,23 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
                 a = fmaf(t, sav[w], a);
               }
             }
-            acc[i] = a;
+            acc[ci][i] = a;
           }
         }
-        if (cp.r == R - 1) {  // item complete: store and restart the accumulators
-          const int tile = cp.tile;
+        if (cp.r == R - 1) {  // item complete: store and restart its accumulators
+          const int tile = cp.tile0 + ci;
 #pragma unroll
           for (int i = 0; i < OPT; ++i) {
             const int o = threadIdx.x + i * THREADS;
             const int n = tile * COLS + o % COLS;
             if (o < OUTS && o / COLS < rows && n < N)
-              y[(size_t)(row0 + o / COLS) * N + n] = float_to_half_bits(acc[i]);
-            acc[i] = 0.0f;
+              y[(size_t)(row0 + o / COLS) * N + n] = float_to_half_bits(acc[ci][i]);
+            acc[ci][i] = 0.0f;
           }
         }
-        cp.next(R, ntiles);
       }
-    }
+      cp.next(C, R, item_end, ntiles);
+    }, std::make_integer_sequence<int, U>{});
   }
 }
 
@@ -242,7 +270,18 @@ int cu_count() {
 
 }  // namespace
 
-template <int MT, int T, int S, int P>
+template <int MT, int T, int S, int P, int C>
+static hipError_t launch_decode_c(const int8_t* qa, const float* sa, const uint32_t* wp,
+                                  const uint16_t* sw, int64_t M, int64_t N, int64_t K,
+                                  uint16_t* y, int64_t ntiles16, int64_t ntiles, int64_t items,
+                                  int64_t per_wg, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_decode_kernel<MT, T, S, P, C>), dim3((unsigned)grid), dim3(64 * S), 0,
+                     stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, y, (int)ntiles16,
+                     (int)ntiles, (int)items, (int)per_wg);
+  return hipGetLastError();
+}
+
+template <int MT, int T, int S, int P, int CMAX>
 static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint32_t* wp,
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                   uint16_t* y, hipStream_t stream) {
@@ -254,10 +293,22 @@ static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint3
   const int64_t grid0 = std::min<int64_t>(items, cu_count());
   const int64_t per_wg = (items + grid0 - 1) / grid0;
   const int64_t grid = (items + per_wg - 1) / per_wg;
-  hipLaunchKernelGGL((gemm_decode_kernel<MT, T, S, P>), dim3((unsigned)grid), dim3(64 * S), 0,
-                     stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, y, (int)ntiles16,
-                     (int)ntiles, (int)items, (int)per_wg);
-  return hipGetLastError();
+  // chunk: the workgroup's items share each round's activation fragments (not worth
+  // the empty steps of a partial chunk when there are only a few token rows)
+  if (M <= 4)
+    return launch_decode_c<MT, T, S, P, 1>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items,
+                                           per_wg, grid, stream);
+  if (CMAX >= 8 && per_wg >= 5)
+    return launch_decode_c<MT, T, S, P, (CMAX >= 8 ? 8 : 1)>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items,
+                                           per_wg, grid, stream);
+  if (CMAX >= 4 && per_wg >= 3)
+    return launch_decode_c<MT, T, S, P, (CMAX >= 4 ? 4 : 1)>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items,
+                                           per_wg, grid, stream);
+  if (CMAX >= 2 && per_wg >= 2)
+    return launch_decode_c<MT, T, S, P, (CMAX >= 2 ? 2 : 1)>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items,
+                                           per_wg, grid, stream);
+  return launch_decode_c<MT, T, S, P, 1>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items,
+                                         per_wg, grid, stream);
 }
 
 hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t* wp,
@@ -265,10 +316,10 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
                               hipStream_t stream) {
   // rows per pass: 16 * MT; more passes over W only when M > 64
   const int64_t rows = M > 64 ? 64 : M;
-  if (rows <= 16) return launch_decode_t<1, 2, 16, 2>(qa, sa, wp, sw, M, N, K, y, stream);
-  if (rows <= 32) return launch_decode_t<2, 2, 16, 2>(qa, sa, wp, sw, M, N, K, y, stream);
-  if (rows <= 48) return launch_decode_t<3, 1, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
-  return launch_decode_t<4, 1, 8, 4>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 16) return launch_decode_t<1, 2, 16, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 32) return launch_decode_t<2, 2, 16, 2, 2>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 48) return launch_decode_t<3, 1, 8, 4, 1>(qa, sa, wp, sw, M, N, K, y, stream);
+  return launch_decode_t<4, 1, 8, 4, 1>(qa, sa, wp, sw, M, N, K, y, stream);
 }
 
 }  // namespace flexq

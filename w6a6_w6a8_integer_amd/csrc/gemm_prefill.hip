@@ -93,11 +93,6 @@ __device__ __forceinline__ void rescale4(float (&a)[16], const f32x16& F, float 
   fmac_row_bcast<R0 + 3>(a[R0 + 3], S, t3);
 }
 
-// f(integral_constant<int, K>) for K = 0 .. n-1, in order.
-template <class F, int... K>
-__device__ __forceinline__ void unroll(F&& f, std::integer_sequence<int, K...>) {
-  (f(std::integral_constant<int, K>{}), ...);
-}
 
 }  // namespace
 

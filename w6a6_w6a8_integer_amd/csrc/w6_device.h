@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace flexq {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -79,6 +81,13 @@ __device__ __forceinline__ i32x4 mfma16(i32x4 a, i32x4 b, i32x4 c) {
 // row 8*(r/4) + 4*(l/32) + r%4.
 __device__ __forceinline__ i32x16 mfma32(i32x4 a, i32x4 b, i32x16 c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// f(integral_constant<int, K>) for K = 0 .. n-1, in order (compile-time indices in
+// unrolled loops).
+template <class F, int... K>
+__device__ __forceinline__ void unroll(F&& f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
 }
 
 }  // namespace flexq
