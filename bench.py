@@ -34,7 +34,7 @@ GROUP = 128
 LAYERS = synth.LLAMA2_70B
 M_LIST = (1, 16, 64, 256, 1024, 4096)
 ABITS = (6, 8)
-DECODE_MAX_M = 32
+DECODE_MAX_M = 64
 
 
 def gemm_bytes(M, N, K):

@@ -80,7 +80,7 @@ typedef enum {
 #define FLEXQ_ABI_VERSION 1
 #define FLEXQ_PACK_FORMAT_VERSION 1
 #define FLEXQ_GROUP_SIZE 128
-#define FLEXQ_DECODE_MAX_M 32
+#define FLEXQ_DECODE_MAX_M 64
 
 /* FLEXQ_ABI_VERSION of the loaded library. */
 int flexq_abi_version(void);

@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libflexq.so")
 
 GROUP = 128
-DECODE_MAX_M = 32
+DECODE_MAX_M = 64
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 
 STATUS_NAMES = {0: "FLEXQ_SUCCESS", 1: "FLEXQ_ERROR_INVALID_VALUE", 2: "FLEXQ_ERROR_UNSUPPORTED",

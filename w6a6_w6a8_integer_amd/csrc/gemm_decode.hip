@@ -318,8 +318,8 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
   const int64_t rows = M > 64 ? 64 : M;
   if (rows <= 16) return launch_decode_t<1, 2, 16, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
   if (rows <= 32) return launch_decode_t<2, 2, 16, 2, 2>(qa, sa, wp, sw, M, N, K, y, stream);
-  if (rows <= 48) return launch_decode_t<3, 1, 8, 4, 1>(qa, sa, wp, sw, M, N, K, y, stream);
-  return launch_decode_t<4, 1, 8, 4, 1>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 48) return launch_decode_t<3, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
+  return launch_decode_t<4, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
 }
 
 }  // namespace flexq
