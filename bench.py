@@ -34,7 +34,6 @@ GROUP = 128
 LAYERS = synth.LLAMA2_70B
 M_LIST = (1, 16, 64, 256, 1024, 4096)
 ABITS = (6, 8)
-DECODE_MAX_M = 64
 
 
 def gemm_bytes(M, N, K):
@@ -204,7 +203,7 @@ def main():
         by = gemm_bytes(M, N, K)
         tot_ops += ops
         gsum = sum(gemm_ms[k])
-        if M <= DECODE_MAX_M:
+        if fq.auto_path(M, N, K) == fq.PATH_DECODE:
             dec_ops += ops * len(gemm_ms[k])
             dec_bytes += by * len(gemm_ms[k])
             dec_ms += gsum
@@ -213,7 +212,7 @@ def main():
             pre_ms += gsum
         shapes.append({
             "layer": name, "M": M, "N": N, "K": K, "abits": ab,
-            "kernel": "decode" if M <= DECODE_MAX_M else "prefill",
+            "kernel": "decode" if fq.auto_path(M, N, K) == fq.PATH_DECODE else "prefill",
             "gemm_us": round(g * 1e3, 2), "quant_us": round(q * 1e3, 2),
             "tops": round(ops / (g * 1e-3) / 1e12, 2),
             "gbs": round(by / (g * 1e-3) / 1e9, 1),
@@ -225,7 +224,8 @@ def main():
     value = tot_ops / (ms_per_step * 1e-3) / 1e12
 
     pre_tops = pre_ops / (pre_ms * 1e-3) / 1e12 if pre_ms else 0.0
-    pre_launches = sum(1 for (M, _, _) in plan if M > DECODE_MAX_M)
+    pre_launches = sum(1 for (M, _, name) in plan
+                       if fq.auto_path(M, *LAYERS[name]) == fq.PATH_PREFILL)
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9 if dec_ms else 0.0
     if pre_ms >= dec_ms:
         # integer ops: the unit is TOP/s against the dense int8 MFMA peak
@@ -241,6 +241,21 @@ def main():
                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
 
+    # the two target rows: HBM fraction over the M <= 16 GEMMs, int8 MFMA fraction over
+    # the M >= 1024 GEMMs (algorithmic bytes / ops over summed event times)
+    def frac_over(sel, num, peak, scale):
+        ks = [k for k in plan if sel(k[0])]
+        tot = sum(num(k) for k in ks) * args.steps
+        ms = sum(sum(gemm_ms[k]) for k in ks)
+        return round(tot / (ms * 1e-3) / scale / peak, 4) if ms else None
+    targets = {
+        "hbm_frac_m_le_16": frac_over(lambda M: M <= 16,
+                                      lambda k: gemm_bytes(k[0], *LAYERS[k[2]]), HBM_PEAK_GBS, 1e9),
+        "int8_frac_m_ge_1024": frac_over(lambda M: M >= 1024,
+                                         lambda k: 2.0 * k[0] * LAYERS[k[2]][0] * LAYERS[k[2]][1],
+                                         INT8_PEAK_TOPS, 1e12),
+    }
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(bufs, m_list, args.cpu_sample_cols, packed, ms_per_step, tot_ops)
@@ -253,7 +268,7 @@ def main():
         "config": {"workload": "llama2_70b_linear_layers_w6a6_w6a8",
                    "layers": {k: list(v) for k, v in LAYERS.items()}, "M": list(m_list),
                    "abits": list(ABITS), "group": GROUP, "step": "quant_act + gemm per (M, abits, layer)"},
-        "roofline": roofline, "roofline_decode": roofline_decode,
+        "roofline": roofline, "roofline_decode": roofline_decode, "targets": targets,
         "cpu_baseline": cpu,
         "timed_region_ms": round(total_ms, 2), "wall_s": round(wall, 2),
         "shapes": shapes,

@@ -72,7 +72,7 @@ typedef enum {
 } flexq_status;
 
 typedef enum {
-  FLEXQ_PATH_AUTO = 0,    /* decode for M <= FLEXQ_DECODE_MAX_M, prefill above */
+  FLEXQ_PATH_AUTO = 0,    /* see flexq_gemm_w6ax_auto_path */
   FLEXQ_PATH_DECODE = 1,  /* HBM-streaming kernel for few tokens (any M is accepted) */
   FLEXQ_PATH_PREFILL = 2  /* MFMA-bound tiled kernel for many tokens (any M is accepted) */
 } flexq_path;
@@ -124,6 +124,13 @@ flexq_status flexq_quant_act(const uint16_t* x_fp16, int64_t M, int64_t K, int32
 flexq_status flexq_gemm_w6ax(const int8_t* q_a, const float* s_a, const uint32_t* w_packed,
                              const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K,
                              int32_t group_size, int32_t abits, uint16_t* y_fp16, void* stream);
+
+/* The kernel FLEXQ_PATH_AUTO runs for an M x N x K product on the current device:
+   FLEXQ_PATH_DECODE (the weight-streaming kernel) for M <= 32, and for
+   M <= FLEXQ_DECODE_MAX_M when the prefill kernel's 128 x 128 tiles would number
+   fewer than the device's compute units; FLEXQ_PATH_PREFILL otherwise.  K does not
+   enter the choice.  Never fails (M <= 0 or N <= 0 report FLEXQ_PATH_DECODE). */
+int flexq_gemm_w6ax_auto_path(int64_t M, int64_t N, int64_t K);
 
 /* flexq_gemm_w6ax with an explicit kernel choice (flexq_path); both kernels accept
    every M and give identical results. */

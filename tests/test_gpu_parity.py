@@ -173,12 +173,13 @@ def run_gemm_case(fq, M, N, K, abits, path, seed=4):
 # (the wide shapes make the decode kernel pair adjacent column tiles, with a
 # half-empty last pair, and give each workgroup 2 to 5 work items, so the items of a
 # workgroup share their activation fragments in chunks of 2, 4 and 8; with 300 rows
-# the chunks are also cut where a workgroup's items cross into the next 64-row pass)
+# the chunks are also cut where a workgroup's items cross into the next 64-row pass.
+# The last two run the prefill kernel's 128- and 256-row tiles on wide N.)
 SHAPES = [(16, 256, 512), (1, 16, 128), (5, 48, 1152), (17, 272, 640), (33, 160, 384),
           (64, 128, 2048), (65, 144, 512), (128, 256, 1024), (130, 400, 768), (257, 96, 256),
           (300, 528, 1280), (1024, 256, 512), (1100, 400, 384), (2048, 128, 1024),
           (7, 16368, 256), (20, 16368, 384), (3, 20480, 384), (9, 40992, 256),
-          (300, 16368, 256)]
+          (300, 16368, 256), (256, 16384, 256), (1024, 8192, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

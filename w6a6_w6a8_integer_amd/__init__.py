@@ -42,6 +42,7 @@ SIGNATURES = {
     "flexq_gemm_w6ax_path": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32,
                                             _P, _P]),
     "flexq_gemm_w6ax_group_dots": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _P, _P]),
+    "flexq_gemm_w6ax_auto_path": (ctypes.c_int, [_I64, _I64, _I64]),
 }
 
 _lib = None
@@ -151,6 +152,12 @@ def gemm_w6ax_group_dots(q_a: torch.Tensor, w_packed: torch.Tensor, N: int,
                                             dots.data_ptr(), _stream(q_a)),
            "flexq_gemm_w6ax_group_dots")
     return dots
+
+
+def auto_path(M: int, N: int, K: int) -> int:
+    """PATH_DECODE or PATH_PREFILL: the kernel PATH_AUTO runs for this shape on the
+    current device (flexq_gemm_w6ax_auto_path)."""
+    return int(lib().flexq_gemm_w6ax_auto_path(M, N, K))
 
 
 class W6AxLinear:

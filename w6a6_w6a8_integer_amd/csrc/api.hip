@@ -153,11 +153,17 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a, const uin
   if (M == 0 || N == 0) return FLEXQ_SUCCESS;
   FLEXQ_TRY(validate_gemm_operands(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16,
                                    (uint64_t)M * N * 2));
-  if (path == FLEXQ_PATH_AUTO) path = M <= FLEXQ_DECODE_MAX_M ? FLEXQ_PATH_DECODE : FLEXQ_PATH_PREFILL;
+  if (path == FLEXQ_PATH_AUTO) path = flexq::auto_gemm_path(M, N);
   hipStream_t s = (hipStream_t)stream;
   if (path == FLEXQ_PATH_DECODE)
     return launched(flexq::launch_gemm_decode(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
   return launched(flexq::launch_gemm_prefill(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
+}
+
+int flexq_gemm_w6ax_auto_path(int64_t M, int64_t N, int64_t K) {
+  (void)K;  // the choice depends on the token count and the layer width only
+  if (M <= 0 || N <= 0) return FLEXQ_PATH_DECODE;
+  return flexq::auto_gemm_path(M, N);
 }
 
 flexq_status flexq_gemm_w6ax(const int8_t* q_a, const float* s_a, const uint32_t* w_packed,

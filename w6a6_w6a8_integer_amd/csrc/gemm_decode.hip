@@ -252,9 +252,7 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
   }
 }
 
-namespace {
-
-int cu_count() {
+int device_cu_count() {
   static int cached[64];  // per device; 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -268,7 +266,14 @@ int cu_count() {
   return cached[dev];
 }
 
-}  // namespace
+int auto_gemm_path(int64_t M, int64_t N) {
+  // Up to 32 tokens the weights are the whole cost: stream them.  From 33 to 64 the
+  // 128 x 128 prefill tile wins where it has a tile for every CU (wide layers); on
+  // narrow layers it would leave CUs idle and the streaming kernel is faster.
+  if (M <= 32) return 1;
+  if (M <= kDecodeRowsPerPass && (N + 127) / 128 < device_cu_count()) return 1;
+  return 2;
+}
 
 template <int MT, int T, int S, int P, int C>
 static hipError_t launch_decode_c(const int8_t* qa, const float* sa, const uint32_t* wp,
@@ -290,7 +295,7 @@ static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint3
   const int64_t items = ntiles * ((M + 63) / 64);
   if (items > INT32_MAX) return hipErrorInvalidValue;  // item indices are 32-bit
   // one resident workgroup per CU; each takes an equal contiguous share of items
-  const int64_t grid0 = std::min<int64_t>(items, cu_count());
+  const int64_t grid0 = std::min<int64_t>(items, device_cu_count());
   const int64_t per_wg = (items + grid0 - 1) / grid0;
   const int64_t grid = (items + per_wg - 1) / per_wg;
   // chunk: the workgroup's items share each round's activation fragments (not worth

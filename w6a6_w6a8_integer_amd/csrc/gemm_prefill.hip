@@ -119,7 +119,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   using C = PrefillCfg<BM>;
   static_assert(C::A_BLOCKS_PER_WAVE == 4, "tile/thread mismatch");
   static_assert(C::B_UNITS * C::THREADS == BN * 8, "B split");
-  static_assert(C::B_UNITS == 2 || C::B_UNITS == 4, "unpack schedule covers 2 or 4 units");
+  static_assert(C::B_UNITS == 2 || C::B_UNITS == 4 || C::B_UNITS == 8, "unpack schedule");
 
   const int G = K >> 7;
   const int tid = threadIdx.x;
@@ -174,9 +174,9 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // (1536 contiguous bytes per tile and group, unit slot j = u_local*16 + n%16).
   // Load i of a lane takes slot (i%2)*64 + lane of tile TPW*w + i/2, so every load
   // instruction reads 768 contiguous bytes; in fragment order that unit lands at
-  // b_lds0 + (i%2)*8192 + (i/2)*256.
+  // b_lds0 + (i%2)*8192 + ((i/2)%2)*256 + (i/4)*1024 (TPW*w is a multiple of TPW).
   constexpr int TPW = (BN / 16) / C::WAVES;
-  static_assert(C::B_UNITS == 2 * TPW && (TPW == 1 || TPW == 2), "B load split");
+  static_assert(C::B_UNITS == 2 * TPW && (TPW == 1 || TPW == 2 || TPW == 4), "B load split");
   const int b_tile0 = wave * TPW;
   const uint32_t b_voff = (uint32_t)b_tile0 * 12u * (uint32_t)K + (uint32_t)lane * 12u;
   auto b_unit_off = [&](int i) -> uint32_t {
@@ -221,7 +221,8 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   };
   // Unpack unit i of a register set, and its weight scale, into the stage at `so`.
   auto fill_unit = [&](int so, const BRegs& r, int i) {
-    *reinterpret_cast<i32x4*>(lds + so + C::A_BYTES + b_lds0 + (i & 1) * 8192 + (i >> 1) * 256) =
+    *reinterpret_cast<i32x4*>(lds + so + C::A_BYTES + b_lds0 + (i & 1) * 8192 +
+                              ((i >> 1) & 1) * 256 + (i >> 2) * 1024) =
         unpack_unit_x4(r.u[i][0], r.u[i][1], r.u[i][2]);
   };
   auto fill_scale = [&](int so, const BRegs& r) {
@@ -394,11 +395,12 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
         rescale4<4 * k>(acc[0][0], F00, s4c[0], -kMagicF * s4c[0], S0);
       else
         rescale4<4 * (k - 4)>(acc[0][1], F01, s4c[1], -kMagicF * s4c[1], S0);
-      // the unpack of group g+1: its units spread over steps, then its scale
-      constexpr int per = C::B_UNITS <= 2 ? 2 : 1;
-      if constexpr (k >= per && k % per == 0 && k / per - 1 < C::B_UNITS)
-        fill_unit(so_next, other, k / per - 1);
-      if constexpr (k == 6) fill_scale(so_next, other);
+      // the unpack of group g+1: unit u at step 1 + 6u/B_UNITS, then its scale
+      unroll([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (k == 1 + (u * 6) / C::B_UNITS) fill_unit(so_next, other, u);
+      }, std::make_integer_sequence<int, C::B_UNITS>{});
+      if constexpr (k == 7) fill_scale(so_next, other);
       __builtin_amdgcn_sched_barrier(0);
     }, std::make_integer_sequence<int, 8>{});
 

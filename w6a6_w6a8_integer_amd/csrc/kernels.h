@@ -27,4 +27,10 @@ hipError_t launch_group_dots(const int8_t* qa, const uint32_t* wp, int64_t M, in
 // passes of this many tokens above it).
 constexpr int64_t kDecodeRowsPerPass = 64;
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+// The kernel the automatic path runs for an M x N product: 1 = decode, 2 = prefill.
+int auto_gemm_path(int64_t M, int64_t N);
+
 }  // namespace flexq
