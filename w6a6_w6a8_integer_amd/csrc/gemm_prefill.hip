@@ -156,9 +156,15 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // once per 16 lanes).  The copy into it is coalesced: DMA instruction i of wave w
   // moves rows R0 = (4w + i) * 8 .. R0 + 7, lane l taking physical chunk l % 8 of row
   // R0 + l / 8, i.e. logical chunk (l % 8) ^ (4 * (i % 2) + l / 16).
+  // The row part of every offset stays in the VGPR operand, which the range check
+  // that zeroes rows >= M covers; the group's column offset (always inside the row)
+  // goes in the scalar offset.
   const uint32_t a_vrow = (uint32_t)(wave * 32 + (lane >> 3)) * (uint32_t)K;
-  const uint32_t a_voff0 = a_vrow + (uint32_t)(((lane & 7) ^ (lane >> 4)) * 16);
-  const uint32_t a_voff1 = a_vrow + (uint32_t)(((lane & 7) ^ (4 + (lane >> 4))) * 16);
+  uint32_t a_voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    a_voff[i] = a_vrow + (uint32_t)(i * 8) * (uint32_t)K +
+                (uint32_t)(((lane & 7) ^ (4 * (i & 1) + (lane >> 4))) * 16);
   // fragment read offsets (32x32x32 operand: row l % 32, logical chunk 2c + l / 32)
   int a_frag[4];
 #pragma unroll
@@ -182,6 +188,9 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   auto b_unit_off = [&](int i) -> uint32_t {
     return (uint32_t)(i >> 1) * 12u * (uint32_t)K + (uint32_t)(i & 1) * 768u;
   };
+  uint32_t b_voff_u[C::B_UNITS];
+#pragma unroll
+  for (int i = 0; i < C::B_UNITS; ++i) b_voff_u[i] = b_voff + b_unit_off(i);
   // s_w: thread t handles column t % 128 (duplicates write identical values)
   const int sw_col = tid % BN;
   const uint32_t sw_voff = (uint32_t)sw_col * 2u;
@@ -198,23 +207,20 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   };
   BRegs breg[2];  // group h lives in set h % 2 from its issue until its fill
 
-  // Register half of group g's reads: packed weights and weight scales.
+  // Prologue reads of group g: packed weights and weight scales into registers, then
+  // activations and activation scales into the stage at byte offset `so`.
   auto issue_regs = [&](int g, BRegs& r) {
-    const uint32_t bo = b_voff + (uint32_t)g * 1536u;
 #pragma unroll
     for (int i = 0; i < C::B_UNITS; ++i)
-      r.u[i] = __builtin_amdgcn_raw_buffer_load_b96(rw, bo + b_unit_off(i), 0, 0);
+      r.u[i] = __builtin_amdgcn_raw_buffer_load_b96(rw, b_voff_u[i], (uint32_t)g * 1536u, 0);
     r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u, 0, 0);
   };
-  // DMA half of group g's reads: activations and activation scales into the stage
-  // at byte offset `so`.
   auto issue_dma = [&](int g, int so) {
     int8_t* la = lds + so;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_ptr_t)(la + (wave * 4 + i) * 1024), 16,
-          ((i & 1) ? a_voff1 : a_voff0) + (uint32_t)g * 128u + (uint32_t)(i * 8) * K, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(la + (wave * 4 + i) * 1024), 16,
+                                               a_voff[i], (uint32_t)g * 128u, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsa, (lds_ptr_t)(la + C::A_BYTES + C::B_BYTES + sa_row0 * 4), 4,
         sa_voff + (uint32_t)g * (uint32_t)M * 4u, 0, 0, 0);
@@ -243,16 +249,16 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   auto vmem_op = [&](auto ic, int g, int so, BRegs& r) {
     constexpr int i = decltype(ic)::value;
     if constexpr (i < 4) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_ptr_t)(lds + so + (wave * 4 + i) * 1024), 16,
-          ((i & 1) ? a_voff1 : a_voff0) + (uint32_t)g * 128u + (uint32_t)(i * 8) * K, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + so + (wave * 4 + i) * 1024),
+                                               16, a_voff[i], (uint32_t)g * 128u, 0, 0);
     } else if constexpr (i == 4) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsa, (lds_ptr_t)(lds + so + C::A_BYTES + C::B_BYTES + sa_row0 * 4), 4,
           sa_voff + (uint32_t)g * (uint32_t)M * 4u, 0, 0, 0);
     } else if constexpr (i < 5 + C::B_UNITS) {
-      r.u[i - 5] = __builtin_amdgcn_raw_buffer_load_b96(
-          rw, b_voff + (uint32_t)g * 1536u + b_unit_off(i - 5), 0, 0);
+      // (the tile part is in the VGPR operand; a group stays inside its tile)
+      r.u[i - 5] = __builtin_amdgcn_raw_buffer_load_b96(rw, b_voff_u[i - 5], (uint32_t)g * 1536u,
+                                                        0);
     } else {
       r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u,
                                                  0, 0);
@@ -278,6 +284,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   i32x16 dprev[2] = {magic, magic};
   float Sprev = 0.0f;
   float s4prev[2] = {0.0f, 0.0f};
+  float bprev[2] = {-0.0f, -0.0f};  // -12582912 * s4prev
 
   // per-lane byte offsets inside a stage
   const int r32 = lane & 31, hl = lane >> 5;
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     float S0, S1, s4c[2];
     const f32x16 Fp0 = __builtin_bit_cast(f32x16, dprev[0]);
     const f32x16 Fp1 = __builtin_bit_cast(f32x16, dprev[1]);
-    const float bp0 = -kMagicF * s4prev[0], bp1 = -kMagicF * s4prev[1];
+    const float bp0 = bprev[0], bp1 = bprev[1];
     const float Sp = Sprev;
 
     a0[0] = ldA(so, 0, 0);
@@ -384,6 +391,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     // ---- row tile 1
     const f32x16 F00 = __builtin_bit_cast(f32x16, d0[0]);
     const f32x16 F01 = __builtin_bit_cast(f32x16, d0[1]);
+    const float bc0 = -kMagicF * s4c[0], bc1 = -kMagicF * s4c[1];
     unroll([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       constexpr int c = k >> 1, tn = k & 1;
@@ -392,9 +400,9 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
       if constexpr (k == 1) a1[3] = ldA(so, 3, 1);
       d1[tn] = mfma32(a1[c], b[c][tn], c == 0 ? magic : d1[tn]);
       if constexpr (k < 4)
-        rescale4<4 * k>(acc[0][0], F00, s4c[0], -kMagicF * s4c[0], S0);
+        rescale4<4 * k>(acc[0][0], F00, s4c[0], bc0, S0);
       else
-        rescale4<4 * (k - 4)>(acc[0][1], F01, s4c[1], -kMagicF * s4c[1], S0);
+        rescale4<4 * (k - 4)>(acc[0][1], F01, s4c[1], bc1, S0);
       // the unpack of group g+1: unit u at step 1 + 6u/B_UNITS, then its scale
       unroll([&](auto uc) {
         constexpr int u = decltype(uc)::value;
@@ -410,6 +418,8 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     Sprev = S1;
     s4prev[0] = s4c[0];
     s4prev[1] = s4c[1];
+    bprev[0] = bc0;
+    bprev[1] = bc1;
 
     // everything issued before this group's loads has landed (group g+1's DMA), and
     // this group's fills and LDS reads are done before anyone passes the barrier
@@ -439,7 +449,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   {
     const f32x16 Fp0 = __builtin_bit_cast(f32x16, dprev[0]);
     const f32x16 Fp1 = __builtin_bit_cast(f32x16, dprev[1]);
-    const float bp0 = -kMagicF * s4prev[0], bp1 = -kMagicF * s4prev[1];
+    const float bp0 = bprev[0], bp1 = bprev[1];
     unroll([&](auto kc) {
       constexpr int q = decltype(kc)::value;
       rescale4<4 * q>(acc[1][0], Fp0, s4prev[0], bp0, Sprev);
