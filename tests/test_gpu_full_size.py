@@ -11,7 +11,8 @@ scales of the sampled rows and its packed weights and scales of the sampled tile
 Shapes: the toy W6A6 layer, LLaMA-2-7B W6A6 (M 1/16/128), LLaMA-2-13B W6A8
 (M 1/64/512), LLaMA-2-70B in W6A6 and W6A8 (M 1/16/64/256/1024/4096), and the
 distinct GEMMs of the 80-layer 70B stack (decode M = 32 and prefill M = 2048 in
-both precisions; the stack repeats these four layer shapes).
+both precisions; the stack repeats these four layer shapes), and one GPU's share of
+the 70B layers under 8-way tensor parallelism.
 """
 import numpy as np
 import pytest
@@ -27,8 +28,14 @@ DEV = "cuda:0"
 G = 128
 
 STACK_70B = {"layers": synth.LLAMA2_70B, "M": (32, 2048), "abits": (6, 8)}
+# One GPU's share of the 70B layers under 8-way tensor parallelism (qkv and gate_up
+# split along N, o and down along K at whole groups): short K loops and narrow N.
+TP8_70B = {"layers": {"qkv": (10240 // 8, 8192), "o": (8192, 8192 // 8),
+                      "gate_up": (57344 // 8, 8192), "down": (8192, 28672 // 8)},
+           "M": (1, 16, 64, 256, 1024, 4096), "abits": (6, 8)}
+EXTRA = {"llama2_70b_stack": STACK_70B, "llama2_70b_tp8_shard": TP8_70B}
 CASES = []
-for wname, wl in list(synth.WORKLOADS.items()) + [("llama2_70b_stack", STACK_70B)]:
+for wname, wl in list(synth.WORKLOADS.items()) + list(EXTRA.items()):
     for lname in wl["layers"]:
         CASES.append((wname, lname))
 
@@ -58,7 +65,7 @@ def sample_tiles(N, rng):
 
 @pytest.mark.parametrize("wname,lname", CASES, ids=[f"{w}-{l}" for w, l in CASES])
 def test_full_size_sampled(fq, wname, lname):
-    wl = STACK_70B if wname == "llama2_70b_stack" else synth.WORKLOADS[wname]
+    wl = EXTRA[wname] if wname in EXTRA else synth.WORKLOADS[wname]
     N, K = wl["layers"][lname]
     seed = synth.derive_seed(synth.BASE_SEED, "full", wname, lname)
     rng = np.random.default_rng(seed & 0xFFFFFFFF)
