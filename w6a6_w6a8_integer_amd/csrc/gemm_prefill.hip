@@ -15,21 +15,26 @@
 //
 // So every output is bit-identical to the sequential definition.
 //
-// Tile: BM x 128 per workgroup, BM/64 x 2 waves, each wave 64 x 64 = 2 x 2 MFMA
-// tiles of 32 x 32, handled as two halves (row tile 0, row tile 1).  The 2 fp32
-// FMAs of the rescale equal the MFMA time of a group at the chip's rates, so the
-// loop is software-pipelined: the MFMAs of one half run while the VALU rescales the
-// other half (the previous group's second half, then this group's first half).
+// Tile: BM x 128 per workgroup (BM = 256 from 1024 tokens, else 128), BM/32 waves,
+// each wave 64 x 64 outputs = 2 x 2 MFMA tiles of 32 x 32, handled as two row
+// tiles.  A group is written out as 16 steps of one MFMA each: the 8 steps of row
+// tile 0 overlap the rescale of the previous group's row tile 1, the 8 steps of row
+// tile 1 the rescale of this group's row tile 0 and the unpack of the next group.
+// The 16 activation scales a lane needs for one 32 x 32 tile arrive in one register
+// (lane 16j + r holds the scale of output register r) and the accumulate is a
+// v_fmac_f32 with DPP row_newbcast:r, which hands lane r of each 16-lane row to
+// the whole row.
 //
-// Staging: a 3-deep LDS ring per group holds the int8 activation tile, the
-// unpacked weight tile (bytes 4*q) and both scale vectors, all in
-// "fragment-linear" order: every 1 KB block is one 32 x 32 MFMA operand with lane
-// l's 16 bytes at offset 16*l, so fills and fragment reads are linear 16-byte
-// accesses.  Activations and activation scales go global -> LDS directly
-// (buffer_load ... lds, no registers); packed weights and weight scales come
-// through registers (two sets) and are unpacked into the ring.  Loads run two
-// groups ahead; one barrier per group, with the counter waits written out so the
-// loads of group g+2 stay in flight across it.
+// Staging: a 3-deep LDS ring per 128-deep group holds the int8 activation tile,
+// the unpacked weight tile (bytes 4*q) and both scale vectors.  The activation
+// tile is row-major with a 16-byte-chunk XOR swizzle (conflict-free fragment
+// reads); the weight tile is "fragment-linear" (every 1 KB block one 32 x 32 MFMA
+// operand, lane l's 16 bytes at 16*l).  Activations and their scales go global ->
+// LDS directly (buffer_load ... lds, no registers); packed weights and weight
+// scales come through registers (two sets) and are unpacked into the ring.  Loads
+// run two groups ahead, one vector-memory instruction per MFMA step; one barrier
+// per group, with the counter waits written out so the loads of group g+2 stay in
+// flight across it.
 //
 // Workgroups are numbered so that the 8 XCDs each take a contiguous run of
 // logical tiles (hardware hands workgroup i to XCD i % 8), and logical tiles run
