@@ -31,8 +31,9 @@
 // reads); the weight tile is "fragment-linear" (every 1 KB block one 32 x 32 MFMA
 // operand, lane l's 16 bytes at 16*l).  Activations and their scales go global ->
 // LDS directly (buffer_load ... lds, no registers); packed weights and weight
-// scales come through registers (two sets) and are unpacked into the ring.  Loads
-// run two groups ahead, one vector-memory instruction per MFMA step; one barrier
+// scales come through registers (two sets) and are unpacked into the ring; each
+// scale vector is loaded by just the waves that cover it.  Loads run two groups
+// ahead, at most one vector-memory instruction per MFMA step; one barrier
 // per group, with the counter waits written out so the loads of group g+2 stay in
 // flight across it.
 //
@@ -177,8 +178,13 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     const int r = lane & 31;
     a_frag[c] = (wm * 64 + r) * 128 + (((2 * c + (lane >> 5)) ^ ((r >> 1) & 7)) * 16);
   }
-  // s_a: waves w and w + SA_WAVES copy the same 64 rows (identical data, so the
-  // duplicate write is harmless and every wave runs the same instruction stream)
+  // Scales: in the main loop only waves 0 .. SA_WAVES-1 copy s_a (64 rows each) and
+  // only the next BN/64 waves load s_w (one column per thread); each global load
+  // instruction costs issue time whatever its size, so no wave loads a copy another
+  // wave already brings.  (The prologue loads them in every wave; duplicates write
+  // identical values.)
+  const bool sa_wave = wave < C::SA_WAVES;
+  const bool sw_wave = wave >= C::SA_WAVES && wave < C::SA_WAVES + BN / 64;
   const int sa_row0 = (wave % C::SA_WAVES) * 64;
   const uint32_t sa_voff = (uint32_t)(sa_row0 + lane) * 4u;
   // B: wave w loads the 16-column tiles TPW*w .. TPW*w + TPW - 1 of the group
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   uint32_t b_voff_u[C::B_UNITS];
 #pragma unroll
   for (int i = 0; i < C::B_UNITS; ++i) b_voff_u[i] = b_voff + b_unit_off(i);
-  // s_w: thread t handles column t % 128 (duplicates write identical values)
+  // s_w: thread t handles column t % 128
   const int sw_col = tid % BN;
   const uint32_t sw_voff = (uint32_t)sw_col * 2u;
   int b_lds0;
@@ -245,8 +251,10 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     for (int i = 0; i < C::B_UNITS; ++i) fill_unit(so, r, i);
     fill_scale(so, r);
   };
-  // vector-memory instructions issued per group: DMA + register loads
+  // vector-memory instructions of one group: DMA + register loads, and the fewest
+  // any wave issues in the main loop (activation blocks and weight units only)
   constexpr int OPS_PER_GROUP = C::B_UNITS + 1 + C::DMA_OPS;
+  constexpr int MIN_OPS_PER_GROUP = C::B_UNITS + C::A_BLOCKS_PER_WAVE;
   // Vector-memory instruction i of group g (DMA blocks, the s_a row, weight units,
   // the weight scale), so a group's reads can be spread over the MFMA steps: issued
   // in one burst by every wave right after a barrier, they queue at the texture unit
@@ -257,16 +265,18 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + so + (wave * 4 + i) * 1024),
                                                16, a_voff[i], (uint32_t)g * 128u, 0, 0);
     } else if constexpr (i == 4) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsa, (lds_ptr_t)(lds + so + C::A_BYTES + C::B_BYTES + sa_row0 * 4), 4,
-          sa_voff + (uint32_t)g * (uint32_t)M * 4u, 0, 0, 0);
+      if (sa_wave)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsa, (lds_ptr_t)(lds + so + C::A_BYTES + C::B_BYTES + sa_row0 * 4), 4,
+            sa_voff + (uint32_t)g * (uint32_t)M * 4u, 0, 0, 0);
     } else if constexpr (i < 5 + C::B_UNITS) {
       // (the tile part is in the VGPR operand; a group stays inside its tile)
       r.u[i - 5] = __builtin_amdgcn_raw_buffer_load_b96(rw, b_voff_u[i - 5], (uint32_t)g * 1536u,
                                                         0);
     } else {
-      r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u,
-                                                 0, 0);
+      if (sw_wave)
+        r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u,
+                                                   0, 0);
     }
   };
   static_assert(C::DMA_OPS == 5, "vmem_op numbering");
@@ -413,7 +423,9 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
         constexpr int u = decltype(uc)::value;
         if constexpr (k == 1 + (u * 6) / C::B_UNITS) fill_unit(so_next, other, u);
       }, std::make_integer_sequence<int, C::B_UNITS>{});
-      if constexpr (k == 7) fill_scale(so_next, other);
+      if constexpr (k == 7) {
+        if (sw_wave) fill_scale(so_next, other);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }, std::make_integer_sequence<int, 8>{});
 
@@ -427,8 +439,10 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     bprev[1] = bc1;
 
     // everything issued before this group's loads has landed (group g+1's DMA), and
-    // this group's fills and LDS reads are done before anyone passes the barrier
-    wait_vm_lgkm0<OPS_PER_GROUP>();
+    // this group's fills and LDS reads are done before anyone passes the barrier.
+    // Waves issue MIN_OPS_PER_GROUP .. OPS_PER_GROUP loads per group; waiting for the
+    // fewest is exact for some and one or two loads early for the others.
+    wait_vm_lgkm0<MIN_OPS_PER_GROUP>();
     barrier();
   };
 
