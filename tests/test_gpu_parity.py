@@ -230,6 +230,25 @@ def test_gemm_deterministic_and_in_bounds(fq):
         assert torch.all(buf[M * N:] == -1)
 
 
+@pytest.mark.parametrize("M,N,K", [(40, 208, 1024), (1100, 144, 384)])
+def test_gemm_output_not_16_byte_aligned(fq, M, N, K):
+    """An output that is only 4-byte aligned (the documented minimum) takes the
+    kernels' element-wise store path; the results and the guard bands around the
+    output are the same as for an aligned one."""
+    x, w = inputs(11, M, N, K)
+    qa, sa = oracle.quant_act(x, 6)
+    wp, sw = oracle.pack_w6(w)
+    y_ref = oracle.gemm_packed(qa, sa, wp, sw, N).view(np.uint16)
+    args = (to_dev(qa), to_dev(gm(sa)), to_dev(wp.view(np.int32)), to_dev(gm(sw)))
+    for path in (1, 2):
+        buf = torch.full((M * N + 4096,), -1, dtype=torch.int16, device=DEV)
+        y = buf[2:2 + M * N].view(torch.float16).view(M, N)   # 4 bytes past a 16-byte boundary
+        assert y.data_ptr() % 16 == 4
+        fq.gemm_w6ax(*args, N, 6, y=y, path=path)
+        assert np.array_equal(u16(y), y_ref)
+        assert torch.all(buf[:2] == -1) and torch.all(buf[2 + M * N:] == -1)
+
+
 def test_end_to_end_layer(fq):
     """fp16 X and W through the three entry points equal the oracle's chain."""
     M, N, K = 24, 320, 1536

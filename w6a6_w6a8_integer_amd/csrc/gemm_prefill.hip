@@ -62,6 +62,7 @@ constexpr int BN = 128;
 constexpr int STAGES = 3;
 constexpr uint32_t kMagic = 0x4B400000u;
 constexpr float kMagicF = 12582912.0f;
+constexpr int kOutPitch = 144;  // bytes per staged output row: 128 + 16 of padding
 
 // s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
 // vmcnt[5:4] in [15:14]).
@@ -124,6 +125,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     const uint16_t* __restrict__ sw, int M, int N, int K, int GM, uint16_t* __restrict__ y) {
   using C = PrefillCfg<BM>;
   static_assert(C::A_BLOCKS_PER_WAVE == 4, "tile/thread mismatch");
+  static_assert(C::WAVES * 64 * kOutPitch <= STAGES * C::STAGE_BYTES, "output staging fits");
   static_assert(C::B_UNITS * C::THREADS == BN * 8, "B split");
   static_assert(C::B_UNITS == 2 || C::B_UNITS == 4 || C::B_UNITS == 8, "unpack schedule");
 
@@ -476,7 +478,38 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     }, std::make_integer_sequence<int, 4>{});
   }
 
-  // epilogue: fp16 stores, column = lane % 32
+  // Epilogue.  With a 16-byte aligned Y, each wave stages its 64 x 64 fp16 outputs
+  // in LDS (its own region, row pitch kOutPitch) and stores every row as 16-byte
+  // chunks: 8 store instructions per lane instead of 64 two-byte ones.  The barrier
+  // lets no wave overwrite a stage while another wave's copies into it may still
+  // land.  (N is a multiple of 16, so an 8-column chunk is wholly inside or outside
+  // the matrix and every row starts 16-byte aligned.)
+  if ((reinterpret_cast<uintptr_t>(y) & 15u) == 0) {
+    barrier();
+    uint8_t* tw = reinterpret_cast<uint8_t*>(lds) + wave * 64 * kOutPitch;
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = tm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          *reinterpret_cast<uint16_t*>(tw + lr * kOutPitch + (tn * 32 + (lane & 31)) * 2) =
+              float_to_half_bits(acc[tm][tn][r]);
+        }
+    __builtin_amdgcn_wave_barrier();
+    const int col = wn * 64 + (lane & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int lr = i * 8 + (lane >> 3);
+      const i32x4 v = *reinterpret_cast<const i32x4*>(tw + lr * kOutPitch + (lane & 7) * 16);
+      const int row = wm * 64 + lr;
+      if (row < mrows && col < ncols)
+        *reinterpret_cast<i32x4*>(y + (size_t)(m0 + row) * N + n0 + col) = v;
+    }
+    return;
+  }
+  // otherwise one fp16 store per output, column = lane % 32
 #pragma unroll
   for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
