@@ -62,7 +62,9 @@ constexpr int BN = 128;
 constexpr int STAGES = 3;
 constexpr uint32_t kMagic = 0x4B400000u;
 constexpr float kMagicF = 12582912.0f;
-constexpr int kOutPitch = 144;  // bytes per staged output row: 128 + 16 of padding
+constexpr int kOutPitch = 144;
+// which scale vector a wave loads in the main loop
+constexpr int kRoleNone = 0, kRoleSa = 1, kRoleSw = 2;  // bytes per staged output row: 128 + 16 of padding
 
 // s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
 // vmcnt[5:4] in [15:14]).
@@ -183,8 +185,9 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // Scales: in the main loop only waves 0 .. SA_WAVES-1 copy s_a (64 rows each) and
   // only the next BN/64 waves load s_w (one column per thread); each global load
   // instruction costs issue time whatever its size, so no wave loads a copy another
-  // wave already brings.  (The prologue loads them in every wave; duplicates write
-  // identical values.)
+  // wave already brings.  The main loop exists once per role (kRoleSa, kRoleSw,
+  // kRoleNone) so that no branch splits it.  (The prologue loads the scales in every
+  // wave; duplicates write identical values.)
   const bool sa_wave = wave < C::SA_WAVES;
   const bool sw_wave = wave >= C::SA_WAVES && wave < C::SA_WAVES + BN / 64;
   const int sa_row0 = (wave % C::SA_WAVES) * 64;
@@ -261,13 +264,14 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // the weight scale), so a group's reads can be spread over the MFMA steps: issued
   // in one burst by every wave right after a barrier, they queue at the texture unit
   // and stall the waves behind them.
-  auto vmem_op = [&](auto ic, int g, int so, BRegs& r) {
+  auto vmem_op = [&](auto role, auto ic, int g, int so, BRegs& r) {
     constexpr int i = decltype(ic)::value;
+    constexpr int kRole = decltype(role)::value;
     if constexpr (i < 4) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + so + (wave * 4 + i) * 1024),
                                                16, a_voff[i], (uint32_t)g * 128u, 0, 0);
     } else if constexpr (i == 4) {
-      if (sa_wave)
+      if constexpr (kRole == kRoleSa)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsa, (lds_ptr_t)(lds + so + C::A_BYTES + C::B_BYTES + sa_row0 * 4), 4,
             sa_voff + (uint32_t)g * (uint32_t)M * 4u, 0, 0, 0);
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
       r.u[i - 5] = __builtin_amdgcn_raw_buffer_load_b96(rw, b_voff_u[i - 5], (uint32_t)g * 1536u,
                                                         0);
     } else {
-      if (sw_wave)
+      if constexpr (kRole == kRoleSw)
         r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u,
                                                    0, 0);
     }
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // of group g+1.  LDS reads run two or more steps ahead of their MFMA; the B
   // fragments stay in registers for both row tiles.  `mine` held group g and now
   // receives group g+2; `other` holds group g+1.
-  auto step_group = [&](int g, int so, int so_next, int so_dma, BRegs& mine,
+  auto step_group = [&](auto role, int g, int so, int so_next, int so_dma, BRegs& mine,
                         const BRegs& other) __attribute__((always_inline)) {
     // group g+2 goes to registers `mine` (unpacked last group) and to the stage
     // group g-1 used, one vector-memory instruction per MFMA step
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     unroll([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       constexpr int c = k >> 1, tn = k & 1;
-      vmem_op(kc, gn, so_dma, mine);
+      vmem_op(role, kc, gn, so_dma, mine);
       if constexpr (k == 0) a0[2] = ldA(so, 2, 0);
       if constexpr (k == 1) b[2][0] = ldB(so, 2, 0);
       if constexpr (k == 2) b[2][1] = ldB(so, 2, 1);
@@ -412,7 +416,8 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     unroll([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       constexpr int c = k >> 1, tn = k & 1;
-      if constexpr (8 + k < OPS_PER_GROUP) vmem_op(std::integral_constant<int, 8 + k>{}, gn, so_dma, mine);
+      if constexpr (8 + k < OPS_PER_GROUP)
+        vmem_op(role, std::integral_constant<int, 8 + k>{}, gn, so_dma, mine);
       if constexpr (k == 0) a1[2] = ldA(so, 2, 1);
       if constexpr (k == 1) a1[3] = ldA(so, 3, 1);
       d1[tn] = mfma32(a1[c], b[c][tn], c == 0 ? magic : d1[tn]);
@@ -426,7 +431,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
         if constexpr (k == 1 + (u * 6) / C::B_UNITS) fill_unit(so_next, other, u);
       }, std::make_integer_sequence<int, C::B_UNITS>{});
       if constexpr (k == 7) {
-        if (sw_wave) fill_scale(so_next, other);
+        if constexpr (decltype(role)::value == kRoleSw) fill_scale(so_next, other);
       }
       __builtin_amdgcn_sched_barrier(0);
     }, std::make_integer_sequence<int, 8>{});
@@ -451,21 +456,29 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // Unrolled by two so each register set is named statically; no branch sits
   // between a load and the unpack that consumes it.  Stage offsets rotate through
   // the three stages.
-  int so = 0, so1 = C::STAGE_BYTES, so2 = 2 * C::STAGE_BYTES;
-  auto rotate = [&]() {
-    const int t = so;
-    so = so1;
-    so1 = so2;
-    so2 = t;
+  auto main_loop = [&](auto role) __attribute__((always_inline)) {
+    int so = 0, so1 = C::STAGE_BYTES, so2 = 2 * C::STAGE_BYTES;
+    auto rotate = [&]() {
+      const int t = so;
+      so = so1;
+      so1 = so2;
+      so2 = t;
+    };
+    int g = 0;
+    for (; g + 1 < G; g += 2) {
+      step_group(role, g, so, so1, so2, breg[0], breg[1]);
+      rotate();
+      step_group(role, g + 1, so, so1, so2, breg[1], breg[0]);
+      rotate();
+    }
+    if (g < G) step_group(role, g, so, so1, so2, breg[0], breg[1]);
   };
-  int g = 0;
-  for (; g + 1 < G; g += 2) {
-    step_group(g, so, so1, so2, breg[0], breg[1]);
-    rotate();
-    step_group(g + 1, so, so1, so2, breg[1], breg[0]);
-    rotate();
-  }
-  if (g < G) step_group(g, so, so1, so2, breg[0], breg[1]);
+  if (sa_wave)
+    main_loop(std::integral_constant<int, kRoleSa>{});
+  else if (sw_wave)
+    main_loop(std::integral_constant<int, kRoleSw>{});
+  else
+    main_loop(std::integral_constant<int, kRoleNone>{});
   wait_vm_lgkm0<0>();  // no copy into LDS may outlive the workgroup
   {
     const f32x16 Fp0 = __builtin_bit_cast(f32x16, dprev[0]);
@@ -531,7 +544,7 @@ static void launch_prefill_t(const int8_t* qa, const float* sa, const uint32_t* 
                              const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                              hipStream_t stream) {
   const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
-  const int GM = 8;
+  const int GM = 4;
   hipLaunchKernelGGL(gemm_prefill_kernel<BM>, dim3((unsigned)(nbm * nbn)), dim3(BM * 2), 0,
                      stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, GM, y);
 }
