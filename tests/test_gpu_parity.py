@@ -120,6 +120,34 @@ def test_quant_act_edge_values(fq, abits):
     assert np.array_equal(qa.cpu().numpy(), qa_ref)
 
 
+@pytest.mark.parametrize("abits", [6, 8])
+def test_quant_act_quotients_on_rounding_boundaries(fq, abits):
+    """Groups whose quotients v / s are exactly k + 1/2 (ties to even) or one fp16
+    step either side of it, where a quotient formed from the reciprocal of the
+    scale lands next to the boundary and the kernel must take the exact one."""
+    qmax = 31 if abits == 6 else 127
+    rows = []
+    for e in (-4, 0, 3):
+        s = 2.0 ** e                        # s = amax / qmax exactly
+        k = np.arange(-qmax, qmax, dtype=np.float64) + 0.5
+        ties = (k * s).astype(np.float16)
+        up = np.nextafter(ties, np.float16(np.inf))
+        down = np.nextafter(ties, np.float16(-np.inf))
+        for vals in (ties, up, down):
+            row = np.zeros(2 * G, dtype=np.float16)
+            row[0] = np.float16(qmax * s)     # the group maximum
+            n = min(len(vals), G - 1)
+            row[1:1 + n] = vals[:n]
+            row[G] = np.float16(qmax * s)
+            row[G + 1:G + 1 + len(vals) - n] = vals[n:]
+            rows.append(row)
+    x = np.stack(rows)
+    qa_ref, sa_ref = oracle.quant_act(x, abits)
+    qa, sa = fq.quant_act(to_dev(x), abits)
+    assert np.array_equal(sa.cpu().numpy().view(np.uint32), gm(sa_ref).view(np.uint32))
+    assert np.array_equal(qa.cpu().numpy(), qa_ref)
+
+
 # ---------------------------------------------------------------------------
 # group dots (unpack + MFMA lane mapping)
 # ---------------------------------------------------------------------------
