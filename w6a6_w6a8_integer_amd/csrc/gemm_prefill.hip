@@ -15,9 +15,9 @@
 //
 // So every output is bit-identical to the sequential definition.
 //
-// Tile: BM x 128 per workgroup (BM = 256 from 1024 tokens, else 128), BM/32 waves,
-// each wave 64 x 64 outputs = 2 x 2 MFMA tiles of 32 x 32, handled as two row
-// tiles.  A group is written out as 16 steps of one MFMA each: the 8 steps of row
+// Tile: BM x 128 per workgroup (BM = 256 or 128, whichever finishes the grid in
+// less time), BM/32 waves, each wave 64 x 64 outputs = 2 x 2 MFMA tiles of
+// 32 x 32, handled as two row tiles.  A group is written out as 16 steps of one MFMA each: the 8 steps of row
 // tile 0 overlap the rescale of the previous group's row tile 1, the 8 steps of row
 // tile 1 the rescale of this group's row tile 0 and the unpack of the next group.
 // The 16 activation scales a lane needs for one 32 x 32 tile arrive in one register
@@ -552,7 +552,15 @@ static void launch_prefill_t(const int8_t* qa, const float* sa, const uint32_t* 
 hipError_t launch_gemm_prefill(const int8_t* qa, const float* sa, const uint32_t* wp,
                                const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                                hipStream_t stream) {
-  if (M >= 1024)
+  // Tile height: the grid runs in rounds of one workgroup per CU, and a round of
+  // 256-row tiles takes about 1.46 times as long as a round of 128-row tiles
+  // (83 vs 57 us per round at K = 8192 on the LLaMA-2-70B shapes), so the taller,
+  // more efficient tile is taken when it needs enough fewer rounds.
+  const int64_t cu = device_cu_count();
+  const int64_t nbn = (N + BN - 1) / BN;
+  const int64_t rounds256 = ((M + 255) / 256 * nbn + cu - 1) / cu;
+  const int64_t rounds128 = ((M + 127) / 128 * nbn + cu - 1) / cu;
+  if (rounds256 * 146 < rounds128 * 100)
     launch_prefill_t<256>(qa, sa, wp, sw, M, N, K, y, stream);
   else
     launch_prefill_t<128>(qa, sa, wp, sw, M, N, K, y, stream);
