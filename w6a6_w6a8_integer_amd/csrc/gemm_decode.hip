@@ -189,7 +189,8 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
           d[t][ms] = mfma16(a_cur[ms][1], b1, d[t][ms]);
         }
       }
-      // park dots (row-major [row][col]) and this group's scales
+      // park dots 4d (row-major [row][col]) and this group's scales, s_w as s_w / 4
+      // (exact), so the fold forms t = RN(d * s_w) as float(4d) * (s_w / 4)
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
             lds_d[slot][wave][(ms * 16 + 4 * (lane >> 4) + i) * COLS + t * 16 + (lane & 15)] =
                 d[t][ms][i];
       if (lane < ROWS) lds_sa[slot][wave][lane] = b.sa;
-      if (lane < COLS) lds_sw[slot][wave][lane] = half_bits_to_float((uint16_t)b.sw);
+      if (lane < COLS) lds_sw[slot][wave][lane] = 0.25f * half_bits_to_float((uint16_t)b.sw);
       // the step P ahead lands in this ring slot; it is the chunk's first item slot
       // exactly when this one is (P is a multiple of C, or C of P)
       load(b, cl, std::integral_constant<bool, ((p + P) % C) == 0>{});
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
 #pragma unroll
             for (int w = 0; w < S; ++w) {
               if (w < ng) {
-                const float t = (float)(dv[w] >> 2) * swv[w];
+                const float t = (float)dv[w] * swv[w];  // float(4d) is exact
                 a = fmaf(t, sav[w], a);
               }
             }

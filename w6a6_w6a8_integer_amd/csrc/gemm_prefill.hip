@@ -60,8 +60,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int BN = 128;
 constexpr int STAGES = 3;
-constexpr uint32_t kMagic = 0x4B400000u;
-constexpr float kMagicF = 12582912.0f;
 constexpr int kOutPitch = 144;
 // which scale vector a wave loads in the main loop
 constexpr int kRoleNone = 0, kRoleSa = 1, kRoleSw = 2;  // bytes per staged output row: 128 + 16 of padding

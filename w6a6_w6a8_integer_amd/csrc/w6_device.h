@@ -24,6 +24,14 @@ constexpr int kGroup = 128;          // K-group of the method (BTC section: 128-
 constexpr int kUnitsPerGroup = 8;    // 16 codes per unit
 constexpr int kUnitDwords = 3;
 
+// MFMA accumulator start for the fused rescale: the float 1.5 * 2^23.  A group's
+// int32 products started from these bits end as the bits of the float
+// F = 12582912 + 4d exactly while |4d| < 2^22 (always: |d| <= 128 * 32 * 127), and
+// fma(F, s / 4, -12582912 * s / 4) is then the single rounding of d * s for any
+// scale s with at most 22 significant bits (fp16 scales have 11).
+constexpr uint32_t kMagic = 0x4B400000u;
+constexpr float kMagicF = 12582912.0f;
+
 // Decode one unit into 16 int8 lanes holding 4*q, code i in byte i.
 __device__ __forceinline__ i32x4 unpack_unit_x4(uint32_t d0, uint32_t d1, uint32_t d2) {
   i32x4 e;
