@@ -35,6 +35,12 @@ HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 GROUP = 128
 LAYERS = synth.LLAMA2_70B
+# one GPU's share of the same layers under 8-way tensor parallelism: qkv and gate_up
+# split along N, o and down along K at whole 128-groups
+LAYERS_TP8 = {"qkv": (10240 // 8, 8192), "o": (8192, 8192 // 8),
+              "gate_up": (57344 // 8, 8192), "down": (8192, 28672 // 8)}
+WORKLOAD_NAMES = {"70b": "llama2_70b_linear_layers_w6a6_w6a8",
+                  "70b_tp8": "llama2_70b_tp8_shard_linear_layers_w6a6_w6a8"}
 M_LIST = (1, 16, 64, 256, 1024, 4096)
 ABITS = (6, 8)
 
@@ -62,6 +68,9 @@ def parse():
     p.add_argument("--cpu-sample-cols", type=int, default=512,
                    help="output columns per GEMM in the oracle's timed sample")
     p.add_argument("--m", type=str, default=None, help="comma list overriding the token counts")
+    p.add_argument("--layers", choices=sorted(WORKLOAD_NAMES), default="70b",
+                   help="70b: the LLaMA-2-70B linear layers (the benchmark's workload); "
+                        "70b_tp8: one GPU's share of them under 8-way tensor parallelism")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="first run one device-to-device copy of this many MiB (the known-size "
                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -109,6 +118,9 @@ def main():
     import torch
     import w6a6_w6a8_integer_amd as fq
 
+    global LAYERS
+    if args.layers == "70b_tp8":
+        LAYERS = LAYERS_TP8
     fq.lib()
     dev = torch.device("cuda:0")
     if args.copy_calibration:
@@ -123,16 +135,21 @@ def main():
     m_list = tuple(int(v) for v in args.m.split(",")) if args.m else M_LIST
     nthreads = synth.default_threads()
 
-    # ---- weights: generated on the host, packed on the GPU, two resident copies
-    # (alternated between passes so no layer is served from the 256 MB MALL)
+    # ---- weights: generated on the host, packed on the GPU, resident copies rotated
+    # between launches so that no layer is served from the 256 MB MALL (at least two
+    # copies and at least 1 GiB of packed weights in all)
     t0 = time.time()
     packed = {}
+    set_bytes = sum(0.75 * N * K for N, K in LAYERS.values())
+    ncopies = max(2, -(-(1 << 30) // int(set_bytes)))
+    if (len(m_list) * len(ABITS) * len(LAYERS)) % ncopies == 0 and ncopies > 2:
+        ncopies += 1  # a step's launch i then meets a different copy in every step
     for li, (name, (N, K)) in enumerate(LAYERS.items()):
         w = synth.weights(synth.derive_seed(args.seed, "70b", name, "w"), N, K, nthreads=nthreads)
         wd = torch.from_numpy(w).to(dev)
         del w
         copies = []
-        for c in range(2):
+        for c in range(ncopies):
             copies.append(fq.pack_w6(wd))
         del wd
         packed[name] = copies
@@ -153,7 +170,10 @@ def main():
     torch.cuda.synchronize()
     log(f"activations ready ({time.time() - t0:.1f} s)")
 
-    plan = [(M, ab, name) for M in m_list for ab in ABITS for name in LAYERS]
+    # Largest M first: while the long prefill launches run, the host queues the rest of
+    # the step, so the short decode launches at the end start back to back and their
+    # events time the GPU, not the host's launch path.
+    plan = [(M, ab, name) for M in sorted(m_list, reverse=True) for ab in ABITS for name in LAYERS]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in plan]
 
@@ -161,7 +181,7 @@ def main():
         for i, (M, ab, name) in enumerate(plan):
             N, K = LAYERS[name]
             _, xd, qa, sa, y = bufs[(M, name)]
-            wp, sw = packed[name][(s * len(plan) + i) % 2]
+            wp, sw = packed[name][(s * len(plan) + i) % ncopies]
             if timed:
                 ev[i][0].record()
             fq.quant_act(xd, ab, q_a=qa, s_a=sa)
@@ -196,9 +216,9 @@ def main():
     ms_per_step_eager = statistics.median(step_ms)
 
     # The same step captured once as a HIP graph and replayed: the kernels and their
-    # arguments are identical (launch i of a step always uses weight copy i % 2), only
-    # the host-side launch gaps between the 96 kernels go.  Per-kernel figures above
-    # come from the eager steps' events.
+    # arguments are the eager step's (launch i reading weight copy i % ncopies), only
+    # the host-side launch gaps between the kernels go.  Per-kernel figures above come
+    # from the eager steps' events.
     graph_ms = None
     if not args.eager:
         graph = torch.cuda.CUDAGraph()
@@ -249,6 +269,7 @@ def main():
             "frac_int8": round(ops / (g * 1e-3) / 1e12 / INT8_PEAK_TOPS, 3),
             "quant_gbs": round(quant_bytes(M, K) / (q * 1e-3) / 1e9, 1),
         })
+    shapes.sort(key=lambda r: (r["M"], r["abits"], list(LAYERS).index(r["layer"])))
     ms_per_step = statistics.median(graph_ms) if graph_ms else ms_per_step_eager
     value = tot_ops / (ms_per_step * 1e-3) / 1e12
 
@@ -296,7 +317,7 @@ def main():
         "ms_per_step_eager": round(ms_per_step_eager, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "llama2_70b_linear_layers_w6a6_w6a8",
+        "config": {"workload": WORKLOAD_NAMES[args.layers], "weight_copies": ncopies,
                    "layers": {k: list(v) for k, v in LAYERS.items()}, "M": list(m_list),
                    "abits": list(ABITS), "group": GROUP, "step": "quant_act + gemm per (M, abits, layer)"},
         "roofline": roofline, "roofline_decode": roofline_decode, "targets": targets,
