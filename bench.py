@@ -112,7 +112,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+              "(sharding over GPUs is designed, not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
