@@ -221,22 +221,27 @@ def main():
     # from the eager steps' events.
     graph_ms = None
     if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step(False, 0)
-        graph.replay()
-        torch.cuda.synchronize()
-        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        wall1 = time.time()
-        for e0, e1 in gev:
-            e0.record()
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step(False, 0)
             graph.replay()
-            e1.record()
-        torch.cuda.synchronize()
-        wall += time.time() - wall1
-        graph_ms = [e0.elapsed_time(e1) for e0, e1 in gev]
-        total_ms += gev[0][0].elapsed_time(gev[-1][1])
+            torch.cuda.synchronize()
+        except RuntimeError as e:  # capture unsupported here: report the eager time
+            log(f"HIP graph capture failed ({e}); value from the launch-by-launch steps")
+            graph = None
+        if graph is not None:
+            gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            wall1 = time.time()
+            for e0, e1 in gev:
+                e0.record()
+                graph.replay()
+                e1.record()
+            torch.cuda.synchronize()
+            wall += time.time() - wall1
+            graph_ms = [e0.elapsed_time(e1) for e0, e1 in gev]
+            total_ms += gev[0][0].elapsed_time(gev[-1][1])
 
     # ---- aggregate
     shapes = []
