@@ -173,13 +173,6 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   for (int i = 0; i < 4; ++i)
     a_voff[i] = a_vrow + (uint32_t)(i * 8) * (uint32_t)K +
                 (uint32_t)(((lane & 7) ^ (4 * (i & 1) + (lane >> 4))) * 16);
-  // fragment read offsets (32x32x32 operand: row l % 32, logical chunk 2c + l / 32)
-  int a_frag[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int r = lane & 31;
-    a_frag[c] = (wm * 64 + r) * 128 + (((2 * c + (lane >> 5)) ^ ((r >> 1) & 7)) * 16);
-  }
   // Scales: in the main loop only waves 0 .. SA_WAVES-1 copy s_a (64 rows each) and
   // only the next BN/64 waves load s_w (one column per thread); each global load
   // instruction costs issue time whatever its size, so no wave loads a copy another
