@@ -40,7 +40,9 @@ LAYERS = synth.LLAMA2_70B
 LAYERS_TP8 = {"qkv": (10240 // 8, 8192), "o": (8192, 8192 // 8),
               "gate_up": (57344 // 8, 8192), "down": (8192, 28672 // 8)}
 WORKLOAD_NAMES = {"70b": "llama2_70b_linear_layers_w6a6_w6a8",
-                  "70b_tp8": "llama2_70b_tp8_shard_linear_layers_w6a6_w6a8"}
+                  "70b_tp8": "llama2_70b_tp8_shard_linear_layers_w6a6_w6a8",
+                  "70b_stack": "llama2_70b_80_layer_stack_w6a6_w6a8"}
+STACK_LAYERS, STACK_A8_LAYERS, STACK_M = 80, 8, (32, 2048)
 M_LIST = (1, 16, 64, 256, 1024, 4096)
 ABITS = (6, 8)
 
@@ -70,7 +72,9 @@ def parse():
     p.add_argument("--m", type=str, default=None, help="comma list overriding the token counts")
     p.add_argument("--layers", choices=sorted(WORKLOAD_NAMES), default="70b",
                    help="70b: the LLaMA-2-70B linear layers (the benchmark's workload); "
-                        "70b_tp8: one GPU's share of them under 8-way tensor parallelism")
+                        "70b_tp8: one GPU's share of them under 8-way tensor parallelism; "
+                        "70b_stack: all 80 decoder layers resident (52 GB packed), a decode "
+                        "pass at M = 32 and a prefill pass at M = 2048, A8 on 8 seeded layers")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="first run one device-to-device copy of this many MiB (the known-size "
                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -132,8 +136,13 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: {n} bytes read, {n} bytes written")
         del src, dst
-    m_list = tuple(int(v) for v in args.m.split(",")) if args.m else M_LIST
+    stack = args.layers == "70b_stack"
+    m_list = tuple(int(v) for v in args.m.split(",")) if args.m else (STACK_M if stack else M_LIST)
     nthreads = synth.default_threads()
+    # the stack's A8 layers: a seeded choice of STACK_A8_LAYERS of the 80 (all four
+    # linears of such a layer take 8-bit activations)
+    a8_layers = set(np.random.default_rng(synth.derive_seed(args.seed, "stack-a8") & 0xFFFFFFFF)
+                    .choice(STACK_LAYERS, STACK_A8_LAYERS, replace=False).tolist()) if stack else set()
 
     # ---- weights: generated on the host, packed on the GPU, resident copies rotated
     # between launches so that no layer is served from the 256 MB MALL (at least two
@@ -144,6 +153,8 @@ def main():
     ncopies = max(2, -(-(1 << 30) // int(set_bytes)))
     if (len(m_list) * len(ABITS) * len(LAYERS)) % ncopies == 0 and ncopies > 2:
         ncopies += 1  # a step's launch i then meets a different copy in every step
+    if stack:
+        ncopies = STACK_LAYERS  # one resident copy per decoder layer (same synthetic values)
     for li, (name, (N, K)) in enumerate(LAYERS.items()):
         w = synth.weights(synth.derive_seed(args.seed, "70b", name, "w"), N, K, nthreads=nthreads)
         wd = torch.from_numpy(w).to(dev)
@@ -173,15 +184,23 @@ def main():
     # Largest M first: while the long prefill launches run, the host queues the rest of
     # the step, so the short decode launches at the end start back to back and their
     # events time the GPU, not the host's launch path.
-    plan = [(M, ab, name) for M in sorted(m_list, reverse=True) for ab in ABITS for name in LAYERS]
+    # Each launch: (M, abits, linear, weight copy or None = rotate through the copies).
+    if stack:
+        plan = [(M, 8 if layer in a8_layers else 6, name, layer)
+                for M in sorted(m_list, reverse=True) for layer in range(STACK_LAYERS)
+                for name in LAYERS]
+    else:
+        plan = [(M, ab, name, None) for M in sorted(m_list, reverse=True) for ab in ABITS
+                for name in LAYERS]
+    keys = sorted({e[:3] for e in plan}, key=lambda k: (-k[0], k[1], list(LAYERS).index(k[2])))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in plan]
 
     def step(timed: bool, s: int):
-        for i, (M, ab, name) in enumerate(plan):
+        for i, (M, ab, name, widx) in enumerate(plan):
             N, K = LAYERS[name]
             _, xd, qa, sa, y = bufs[(M, name)]
-            wp, sw = packed[name][(s * len(plan) + i) % ncopies]
+            wp, sw = packed[name][widx if widx is not None else (s * len(plan) + i) % ncopies]
             if timed:
                 ev[i][0].record()
             fq.quant_act(xd, ab, q_a=qa, s_a=sa)
@@ -195,8 +214,8 @@ def main():
         step(False, s)
     torch.cuda.synchronize()
 
-    quant_ms = {k: [] for k in plan}
-    gemm_ms = {k: [] for k in plan}
+    quant_ms = {k: [] for k in keys}
+    gemm_ms = {k: [] for k in keys}
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     step_ms = []
     torch.cuda.synchronize()
@@ -205,9 +224,9 @@ def main():
     for s in range(args.steps):
         step(True, s)
         torch.cuda.synchronize()  # read this step's events; the region stays back to back
-        for i, k in enumerate(plan):
-            quant_ms[k].append(ev[i][0].elapsed_time(ev[i][1]))
-            gemm_ms[k].append(ev[i][1].elapsed_time(ev[i][2]))
+        for i, e in enumerate(plan):
+            quant_ms[e[:3]].append(ev[i][0].elapsed_time(ev[i][1]))
+            gemm_ms[e[:3]].append(ev[i][1].elapsed_time(ev[i][2]))
         step_ms.append(ev[0][0].elapsed_time(ev[-1][2]))
     stop.record()
     torch.cuda.synchronize()
@@ -248,14 +267,15 @@ def main():
     tot_ops = 0.0
     dec_ops = dec_bytes = dec_ms = 0.0
     pre_ops = pre_ms = 0.0
-    for k in plan:
+    for e in plan:
+        tot_ops += 2.0 * e[0] * LAYERS[e[2]][0] * LAYERS[e[2]][1]
+    for k in keys:
         M, ab, name = k
         N, K = LAYERS[name]
         g = statistics.median(gemm_ms[k])
         q = statistics.median(quant_ms[k])
         ops = 2.0 * M * N * K
         by = gemm_bytes(M, N, K)
-        tot_ops += ops
         gsum = sum(gemm_ms[k])
         if fq.auto_path(M, N, K) == fq.PATH_DECODE:
             dec_ops += ops * len(gemm_ms[k])
@@ -273,13 +293,14 @@ def main():
             "frac_hbm": round(by / (g * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
             "frac_int8": round(ops / (g * 1e-3) / 1e12 / INT8_PEAK_TOPS, 3),
             "quant_gbs": round(quant_bytes(M, K) / (q * 1e-3) / 1e9, 1),
+            "launches_per_step": len(gemm_ms[k]) // len(step_ms),
         })
     shapes.sort(key=lambda r: (r["M"], r["abits"], list(LAYERS).index(r["layer"])))
     ms_per_step = statistics.median(graph_ms) if graph_ms else ms_per_step_eager
     value = tot_ops / (ms_per_step * 1e-3) / 1e12
 
     pre_tops = pre_ops / (pre_ms * 1e-3) / 1e12 if pre_ms else 0.0
-    pre_launches = sum(1 for (M, _, name) in plan
+    pre_launches = sum(1 for (M, _, name, _) in plan
                        if fq.auto_path(M, *LAYERS[name]) == fq.PATH_PREFILL)
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9 if dec_ms else 0.0
     if pre_ms >= dec_ms:
@@ -299,8 +320,8 @@ def main():
     # the two target rows: HBM fraction over the M <= 16 GEMMs, int8 MFMA fraction over
     # the M >= 1024 GEMMs (algorithmic bytes / ops over summed event times)
     def frac_over(sel, num, peak, scale):
-        ks = [k for k in plan if sel(k[0])]
-        tot = sum(num(k) for k in ks) * args.steps
+        ks = [k for k in keys if sel(k[0])]
+        tot = sum(num(k) * len(gemm_ms[k]) for k in ks)
         ms = sum(sum(gemm_ms[k]) for k in ks)
         return round(tot / (ms * 1e-3) / scale / peak, 4) if ms else None
     targets = {
@@ -313,7 +334,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(bufs, m_list, args.cpu_sample_cols, packed, ms_per_step, tot_ops)
+        per_step = {k: len(gemm_ms[k]) // len(step_ms) for k in keys}
+        cpu = cpu_baseline(bufs, per_step, args.cpu_sample_cols, packed, ms_per_step, tot_ops)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
@@ -323,6 +345,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.layers], "weight_copies": ncopies,
+                   **({"stack_layers": STACK_LAYERS, "a8_layers": sorted(a8_layers)} if stack else {}),
                    "layers": {k: list(v) for k, v in LAYERS.items()}, "M": list(m_list),
                    "abits": list(ABITS), "group": GROUP, "step": "quant_act + gemm per (M, abits, layer)"},
         "roofline": roofline, "roofline_decode": roofline_decode, "targets": targets,
@@ -333,11 +356,12 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(bufs, m_list, cols, packed, gpu_ms_per_step, tot_ops):
-    """The oracle, as it is, on a bounded sample of the same step: full activation
-    quantization of every (M, layer) input, and every GEMM restricted to its first
-    `cols` output columns; the GEMM time is scaled linearly in N (exact: the work
-    is linear in N) to estimate the oracle's time for the whole step."""
+def cpu_baseline(bufs, per_step, cols, packed, gpu_ms_per_step, tot_ops):
+    """The oracle, as it is, on a bounded sample of the same step: for every distinct
+    (M, abits, layer) of the step, the full activation quantization, and the GEMM
+    restricted to its first `cols` output columns; the GEMM time is scaled linearly
+    in N (exact: the work is linear in N) and each shape's time by the number of
+    times a step runs it, to estimate the oracle's time for the whole step."""
     import oracle
     import torch
 
@@ -353,24 +377,26 @@ def cpu_baseline(bufs, m_list, cols, packed, gpu_ms_per_step, tot_ops):
         wps = wp[: n * K * 3 // 16].cpu().numpy().view(np.uint32)  # first n/16 tiles
         sws = np.ascontiguousarray(sw[:, :n].cpu().numpy().T)      # [n][G] for the oracle
         wq[name] = (oracle.unpack_codes(wps, n, K), sws, n)
-    for M in m_list:
-        for ab in ABITS:
-            for name, (N, K) in LAYERS.items():
-                x = bufs[(M, name)][0]
-                t = time.perf_counter()
-                qa, sa = oracle.quant_act(x, ab)
-                q_time += time.perf_counter() - t
-                qw, sws, n = wq[name]
-                t = time.perf_counter()
-                oracle.gemm(qa, sa, qw, sws, nthreads=threads)
-                dt = time.perf_counter() - t
-                g_time += dt
-                g_time_scaled += dt * (N / n)
-                sample_ops += 2.0 * M * n * K
-    est_step_s = q_time + g_time_scaled
+    q_time_step = 0.0
+    for (M, ab, name), count in per_step.items():
+        N, K = LAYERS[name]
+        x = bufs[(M, name)][0]
+        t = time.perf_counter()
+        qa, sa = oracle.quant_act(x, ab)
+        dq = time.perf_counter() - t
+        q_time += dq
+        q_time_step += dq * count
+        qw, sws, n = wq[name]
+        t = time.perf_counter()
+        oracle.gemm(qa, sa, qw, sws, nthreads=threads)
+        dt = time.perf_counter() - t
+        g_time += dt
+        g_time_scaled += dt * (N / n) * count
+        sample_ops += 2.0 * M * n * K
+    est_step_s = q_time_step + g_time_scaled
     return {"value": round(tot_ops / est_step_s / 1e12, 5), "unit": "TOPS", "cores": threads,
             "kind": "oracle",
-            "sample": (f"every (M, abits, layer) of the step: full activation quantization "
+            "sample": (f"every distinct (M, abits, layer) of the step: full activation quantization "
                        f"({q_time:.1f} s, 1 thread) and the GEMM on the first {cols} output "
                        f"columns ({g_time:.1f} s, {threads} threads), GEMM time scaled by N/{cols}; "
                        f"estimated oracle step {est_step_s:.0f} s vs GPU {gpu_ms_per_step:.2f} ms"),
