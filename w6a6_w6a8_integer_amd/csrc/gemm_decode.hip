@@ -331,7 +331,12 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
       return launch_decode_t<1, 1, 16, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
     return launch_decode_t<1, 2, 16, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
   }
-  if (rows <= 32) return launch_decode_t<2, 2, 16, 2, 2>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 32) {
+    // single tiles on narrow, short layers as above; then chunks of up to 4 items
+    if (N / 16 <= 3 * (int64_t)device_cu_count() && K <= 16384)
+      return launch_decode_t<2, 1, 16, 2, 4>(qa, sa, wp, sw, M, N, K, y, stream);
+    return launch_decode_t<2, 2, 16, 2, 2>(qa, sa, wp, sw, M, N, K, y, stream);
+  }
   if (rows <= 48) return launch_decode_t<3, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
   return launch_decode_t<4, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
 }
