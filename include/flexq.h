@@ -139,6 +139,31 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a,
                                   int64_t M, int64_t N, int64_t K, int32_t group_size,
                                   int32_t abits, int32_t path, uint16_t* y_fp16, void* stream);
 
+/* Bytes of workspace flexq_linear_w6ax needs for an M x K activation: q_a (M*K
+   bytes, rounded up to a multiple of 256) followed by s_a (M*(K/128)*4 bytes).
+   Returns 0 for M <= 0, K <= 0 or K not a multiple of 128. */
+size_t flexq_linear_w6ax_workspace_bytes(int64_t M, int64_t K);
+
+/* One W6A6 / W6A8 linear layer from fp16 activations in one call: flexq_quant_act
+   into the workspace, then flexq_gemm_w6ax with the automatic kernel choice (blog,
+   "Bridging Software and Hardware with BTC": quantized operands feed the integer
+   GEMM; FlexQ abstract: activations at 6 or 8 bits).  Y is bit-identical to those
+   two calls.  Nothing is allocated, so the call can be captured in a HIP graph.
+     x_fp16    [M][K] fp16, 16-byte aligned (input)
+     w_packed, s_w_fp16 as for flexq_gemm_w6ax (input)
+     workspace device memory of at least flexq_linear_w6ax_workspace_bytes(M, K)
+               bytes, 16-byte aligned; owned by the caller.  Its contents are
+               overwritten (q_a, then s_a) and it must not be used by other work
+               until this call's kernels have run.
+     y_fp16    [M][N] fp16, 4-byte aligned (output)
+   M == 0 or N == 0 is a no-op.  Errors: INVALID_VALUE (null, negative size, abits,
+   workspace too small, overlap of any two of x, weights, workspace and y),
+   UNSUPPORTED (group_size, K % 128, N % 16, size limits, alignment). */
+flexq_status flexq_linear_w6ax(const uint16_t* x_fp16, const uint32_t* w_packed,
+                               const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K,
+                               int32_t group_size, int32_t abits, void* workspace,
+                               size_t workspace_bytes, uint16_t* y_fp16, void* stream);
+
 /* The int32 group dots d[m][n][g] (the integer products of the BTC section) computed
    with the same weight unpack and int8 MFMA as the GEMM; for verification.
      dots [M][N][K/128] int32, 4-byte aligned (output). */

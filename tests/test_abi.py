@@ -130,6 +130,49 @@ def test_group_dots_rejects_bad_arguments(flexq):
     assert f(None, None, 0, 16, 128, 128, None, None) == SUCCESS
 
 
+def test_linear_workspace_bytes(flexq):
+    f = flexq.flexq_linear_w6ax_workspace_bytes
+    assert f(1, 128) == 256 + 4         # q_a 128 B rounded up to 256, then s_a
+    assert f(5, 128) == 768 + 5 * 4
+    assert f(3, 8192) == 24576 + 3 * 64 * 4
+    assert f(4096, 8192) == 4096 * 8192 + 4096 * 64 * 4
+    assert f(0, 128) == 0 and f(-3, 128) == 0 and f(8, 100) == 0 and f(8, 0) == 0
+
+
+def test_linear_rejects_bad_arguments(flexq):
+    f = flexq.flexq_linear_w6ax
+    ws = 6 * A16
+    need = flexq.flexq_linear_w6ax_workspace_bytes(8, 128)
+
+    def call(M=8, N=16, K=128, group=128, abits=6, x=A16, wp=3 * A16, sw=4 * A16, y=5 * A16,
+             w=ws, wb=need):
+        return f(x, wp, sw, M, N, K, group, abits, w, wb, y, None)
+
+    assert call(abits=5) == INVALID
+    assert call(x=None) == INVALID
+    assert call(wp=None) == INVALID
+    assert call(sw=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(M=-1) == INVALID
+    assert call(K=0) == INVALID
+    assert call(K=192) == UNSUPPORTED
+    assert call(N=40) == UNSUPPORTED
+    assert call(group=64) == UNSUPPORTED
+    assert call(x=A16 + 8) == UNSUPPORTED
+    assert call(wp=3 * A16 + 4) == UNSUPPORTED
+    assert call(y=5 * A16 + 2) == UNSUPPORTED
+    assert call(y=A16 + 64) == INVALID               # Y overlaps X
+    assert call(y=3 * A16 + 16) == INVALID           # Y overlaps the packed weight
+    assert call(w=None) == INVALID
+    assert call(wb=need - 1) == INVALID              # workspace too small
+    assert call(w=ws + 8) == UNSUPPORTED             # workspace not 16-byte aligned
+    assert call(w=A16 + 16) == INVALID               # workspace overlaps X
+    assert call(w=5 * A16) == INVALID                # workspace overlaps Y
+    assert call(w=4 * A16) == INVALID                # workspace overlaps s_w
+    assert call(M=0, x=None, y=None, w=None, wb=0) == SUCCESS
+    assert call(N=0, wp=None, y=None, w=None, wb=0) == SUCCESS
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import w6a6_w6a8_integer_amd as fq

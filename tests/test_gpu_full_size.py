@@ -7,6 +7,8 @@ depends only on its own token row and weight row: a sample of rows and 16-column
 tiles is quantized and multiplied by the oracle alone and compared bit for bit with
 the GPU's outputs at those positions, together with the GPU's activation codes and
 scales of the sampled rows and its packed weights and scales of the sampled tiles.
+At M = 1 the one-call layer (flexq_linear_w6ax) must also give the two-call result
+in full, bit for bit.
 
 Shapes: the toy W6A6 layer, LLaMA-2-7B W6A6 (M 1/16/128), LLaMA-2-13B W6A8
 (M 1/64/512), LLaMA-2-70B in W6A6 and W6A8 (M 1/16/64/256/1024/4096), and the
@@ -95,6 +97,9 @@ def test_full_size_sampled(fq, wname, lname):
             say(f"{wname} {lname} M={M} N={N} K={K} abits={abits}")
             qa, sa = fq.quant_act(xd, abits)
             y = fq.gemm_w6ax(qa, sa, wp, sw, N, abits)
+            if M == 1:
+                y_lin = fq.linear_w6ax(xd, wp, sw, N, abits)
+                assert torch.equal(y_lin.view(torch.int16), y.view(torch.int16))
             torch.cuda.synchronize()
             qa_ref, sa_ref = oracle.quant_act(np.ascontiguousarray(x[rows]), abits)
             assert np.array_equal(qa[torch.from_numpy(rows).to(DEV)].cpu().numpy(), qa_ref)

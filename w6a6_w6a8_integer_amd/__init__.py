@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
 * :func:`pack_w6`        fp16 W[N][K] -> packed 6-bit codes + fp16 group scales
 * :func:`quant_act`      fp16 X[M][K] -> int8 codes (INT6 or INT8 range) + fp32 scales
 * :func:`gemm_w6ax`      Y[M][N] fp16 = sum over groups of int32 dot x s_w x s_a
+* :func:`linear_w6ax`    Y[M][N] fp16 from fp16 X in one call (both kernels, q_a / s_a
+  in a caller-supplied or binding-allocated workspace)
 * :func:`gemm_w6ax_group_dots`  the int32 group dots (verification)
 """
 from __future__ import annotations
@@ -43,6 +45,9 @@ SIGNATURES = {
                                             _P, _P]),
     "flexq_gemm_w6ax_group_dots": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _P, _P]),
     "flexq_gemm_w6ax_auto_path": (ctypes.c_int, [_I64, _I64, _I64]),
+    "flexq_linear_w6ax_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "flexq_linear_w6ax": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P,
+                                         ctypes.c_size_t, _P, _P]),
 }
 
 _lib = None
@@ -141,6 +146,30 @@ def gemm_w6ax(q_a: torch.Tensor, s_a: torch.Tensor, w_packed: torch.Tensor, s_w:
     return y
 
 
+def linear_w6ax_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().flexq_linear_w6ax_workspace_bytes(M, K))
+
+
+def linear_w6ax(x: torch.Tensor, w_packed: torch.Tensor, s_w: torch.Tensor, N: int, abits: int,
+                y: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Y fp16[M][N] from fp16 X[M][K] and packed weights (flexq_linear_w6ax); the
+    workspace (uint8, at least linear_w6ax_workspace_bytes(M, K)) is allocated here
+    when the caller does not pass one."""
+    _cuda(x, torch.float16, "x")
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, linear_w6ax_workspace_bytes(M, K)), dtype=torch.uint8,
+                                device=x.device)
+    ws_ptr = workspace.data_ptr()
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().flexq_linear_w6ax(x.data_ptr(), w_packed.data_ptr(), s_w.data_ptr(), M, N, K,
+                                   GROUP, abits, ws_ptr, ws_bytes, y.data_ptr(), _stream(x)),
+           "flexq_linear_w6ax")
+    return y
+
+
 def gemm_w6ax_group_dots(q_a: torch.Tensor, w_packed: torch.Tensor, N: int,
                          dots: torch.Tensor | None = None):
     """int32 d[M][N][K/128] through the production unpack + int8 MFMA."""
@@ -170,5 +199,7 @@ class W6AxLinear:
         self.w_packed, self.s_w = pack_w6(weight_fp16.contiguous())
 
     def __call__(self, x_fp16: torch.Tensor, path: int = PATH_AUTO) -> torch.Tensor:
+        if path == PATH_AUTO:
+            return linear_w6ax(x_fp16.contiguous(), self.w_packed, self.s_w, self.N, self.abits)
         q_a, s_a = quant_act(x_fp16.contiguous(), self.abits)
         return gemm_w6ax(q_a, s_a, self.w_packed, self.s_w, self.N, self.abits, path=path)

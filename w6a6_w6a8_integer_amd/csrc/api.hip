@@ -173,6 +173,51 @@ flexq_status flexq_gemm_w6ax(const int8_t* q_a, const float* s_a, const uint32_t
                               FLEXQ_PATH_AUTO, y_fp16, stream);
 }
 
+size_t flexq_linear_w6ax_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % kGroup != 0) return 0;
+  return ((size_t)M * (size_t)K + 255) / 256 * 256 + (size_t)M * (size_t)(K / kGroup) * 4;
+}
+
+flexq_status flexq_linear_w6ax(const uint16_t* x_fp16, const uint32_t* w_packed,
+                               const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K,
+                               int32_t group_size, int32_t abits, void* workspace,
+                               size_t workspace_bytes, uint16_t* y_fp16, void* stream) {
+  FLEXQ_TRY(check_m(M));
+  FLEXQ_TRY(check_n(N));
+  FLEXQ_TRY(check_k(K, group_size));
+  FLEXQ_TRY(check_scales(M, K));
+  FLEXQ_TRY(check_scales(N, K));
+  if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return FLEXQ_SUCCESS;
+  if (!x_fp16 || !w_packed || !s_w_fp16 || !y_fp16) return FLEXQ_ERROR_INVALID_VALUE;
+  if (!aligned(x_fp16, 16) || !aligned(w_packed, 16) || !aligned(s_w_fp16, 2) ||
+      !aligned(y_fp16, 4))
+    return FLEXQ_ERROR_UNSUPPORTED;
+  const size_t ws = flexq_linear_w6ax_workspace_bytes(M, K);
+  if (!workspace || workspace_bytes < ws) return FLEXQ_ERROR_INVALID_VALUE;
+  if (!aligned(workspace, 16)) return FLEXQ_ERROR_UNSUPPORTED;
+  const uint64_t G = (uint64_t)(K / kGroup);
+  const Range rx = range_of(x_fp16, (uint64_t)M * K * 2);
+  const Range rw = range_of(w_packed, (uint64_t)N * K * 3 / 4);
+  const Range rs = range_of(s_w_fp16, (uint64_t)N * G * 2);
+  const Range ry = range_of(y_fp16, (uint64_t)M * N * 2);
+  const Range rk = range_of(workspace, ws);
+  if (overlap(ry, rx) || overlap(ry, rw) || overlap(ry, rs))
+    return FLEXQ_ERROR_INVALID_VALUE;
+  if (overlap(rk, rx) || overlap(rk, rw) || overlap(rk, rs) || overlap(rk, ry))
+    return FLEXQ_ERROR_INVALID_VALUE;
+  const int qmax = abits == 6 ? 31 : 127;
+  hipStream_t s = (hipStream_t)stream;
+  int8_t* q_a = static_cast<int8_t*>(workspace);
+  float* s_a = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        ((size_t)M * (size_t)K + 255) / 256 * 256);
+  FLEXQ_TRY(launched(flexq::launch_quant_act(x_fp16, M, K, qmax, q_a, s_a, s)));
+  const int path = flexq::auto_gemm_path(M, N);
+  if (path == FLEXQ_PATH_DECODE)
+    return launched(flexq::launch_gemm_decode(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
+  return launched(flexq::launch_gemm_prefill(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
+}
+
 flexq_status flexq_gemm_w6ax_group_dots(const int8_t* q_a, const uint32_t* w_packed, int64_t M,
                                         int64_t N, int64_t K, int32_t group_size, int32_t* dots,
                                         void* stream) {

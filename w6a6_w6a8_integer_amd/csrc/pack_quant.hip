@@ -56,31 +56,6 @@ __global__ __launch_bounds__(128) void pack_w6_kernel(const uint16_t* __restrict
 
 // Thread = 8 consecutive activations; 16 adjacent lanes (one DPP row) = one
 // 128-deep group.  blockIdx.x = token row, blockIdx.y = chunk of 2048 columns.
-// max over the 16 lanes of a DPP row (butterfly: swap pairs, swap pairs of pairs,
-// mirror within 8 lanes, mirror within 16 lanes)
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)));
-  return x;
-}
-
-// Code of one activation: rint(RN(v / s)) clamped to +-qmax, s > 0.  The quotient
-// is first taken as q = RN(v * r) with r = RN(1 / s); |v / s| <= 128, so q is within
-// 2^-16 of v / s, and the correctly rounded quotient within 2^-17 of it.  When q
-// is at least 2^-15 away from the nearest odd multiple of 1/2 (the rounding
-// boundaries), both round to the same integer; otherwise (a few activations in ten
-// thousand on typical inputs) the exact quotient is formed.  Every step of the test is exact: q - rint(q)
-// and its distance to 1/2 are differences of nearby fp32 values.
-__device__ __forceinline__ int quant_code(float v, float s, float r, int qmax) {
-  const float q = v * r;
-  float k = rintf(q);
-  if (fabsf(fabsf(q - k) - 0.5f) < 0x1p-15f) k = rintf(v / s);
-  const int c = (int)k;
-  return c > qmax ? qmax : (c < -qmax ? -qmax : c);
-}
-
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int M,
                                                         int K, int qmax, int8_t* __restrict__ qa,
                                                         float* __restrict__ sa) {
@@ -88,32 +63,9 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
   const int k0 = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (k0 >= K) return;  // whole groups drop out together (K % 128 == 0)
   const u32x4 h = *reinterpret_cast<const u32x4*>(x + m * K + k0);
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = half_bits_to_float((uint16_t)(h[i] & 0xFFFFu));
-    v[2 * i + 1] = half_bits_to_float((uint16_t)(h[i] >> 16));
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = row16_max(amax);
-  const float s = amax / (float)qmax;  // +0 when the group is all zero
-  const float r = 1.0f / s;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = s != 0.0f ? quant_code(v[i], s, r, qmax) : 0;
-    const uint32_t b = (uint32_t)(c & 0xFF);
-    if (i < 4)
-      lo |= b << (8 * i);
-    else
-      hi |= b << (8 * (i - 4));
-  }
-  u32x2 out;
-  out[0] = lo;
-  out[1] = hi;
-  *reinterpret_cast<u32x2*>(qa + m * K + k0) = out;
+  float s;
+  const u32x2 codes = quant8_row16(h, qmax, s);
+  *reinterpret_cast<u32x2*>(qa + m * K + k0) = codes;
   if ((threadIdx.x & 15) == 0) sa[(int64_t)(k0 >> 7) * M + m] = s;  // group-major scales
 }
 

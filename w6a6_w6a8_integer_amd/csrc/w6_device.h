@@ -78,6 +78,58 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32
 }
 
+// max over the 16 lanes of a DPP row (butterfly: swap pairs, swap pairs of pairs,
+// mirror within 8 lanes, mirror within 16 lanes)
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)));
+  return x;
+}
+
+// Code of one activation: rint(RN(v / s)) clamped to +-qmax, s > 0.  The quotient
+// is first taken as q = RN(v * r) with r = RN(1 / s); |v / s| <= 128, so q is within
+// 2^-16 of v / s, and the correctly rounded quotient within 2^-17 of it.  When q
+// is at least 2^-15 away from the nearest odd multiple of 1/2 (the rounding
+// boundaries), both round to the same integer; otherwise (a few activations in ten
+// thousand on typical inputs) the exact quotient is formed.  Every step of the test is exact: q - rint(q)
+// and its distance to 1/2 are differences of nearby fp32 values.
+__device__ __forceinline__ int quant_code(float v, float s, float r, int qmax) {
+  const float q = v * r;
+  float k = rintf(q);
+  if (fabsf(fabsf(q - k) - 0.5f) < 0x1p-15f) k = rintf(v / s);
+  const int c = (int)k;
+  return c > qmax ? qmax : (c < -qmax ? -qmax : c);
+}
+
+// Activation group quantization, one lane's share: 8 consecutive fp16 activations
+// of a 128-deep group whose other 120 sit in the other 15 lanes of this lane's DPP
+// row.  Returns the 8 int8 codes (byte i = code i) and sets s to the group's scale
+// amax / qmax (+0 for an all-zero group, whose codes are 0).  Every lane of the
+// wave must take part (the group max is a DPP butterfly).
+__device__ __forceinline__ u32x2 quant8_row16(const u32x4 h, int qmax, float& s) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = half_bits_to_float((uint16_t)(h[i] & 0xFFFFu));
+    v[2 * i + 1] = half_bits_to_float((uint16_t)(h[i] >> 16));
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = row16_max(amax);
+  s = amax / (float)qmax;
+  const float r = 1.0f / s;
+  u32x2 out = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = s != 0.0f ? quant_code(v[i], s, r, qmax) : 0;
+    out[i >> 2] |= (uint32_t)(c & 0xFF) << (8 * (i & 3));
+  }
+  return out;
+}
+
 // 16x16x64 int8 MFMA: lane l supplies A row (l % 16) and B column (l % 16), 16 bytes
 // each, for k-block (l / 16); D lane l holds column l % 16, rows 4*(l/16) .. +3.
 __device__ __forceinline__ i32x4 mfma16(i32x4 a, i32x4 b, i32x4 c) {
