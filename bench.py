@@ -47,6 +47,9 @@ M_LIST = (1, 16, 64, 256, 1024, 4096)
 ABITS = (6, 8)
 
 
+TILE_NAMES = {3: "256x128", 4: "128x128", 5: "128x64"}
+
+
 def gemm_bytes(M, N, K):
     """Algorithmic HBM bytes of one GEMM: packed W + fp16 s_w + int8 q_a + fp32 s_a + fp16 Y."""
     G = K // GROUP
@@ -287,6 +290,8 @@ def main():
         shapes.append({
             "layer": name, "M": M, "N": N, "K": K, "abits": ab,
             "kernel": "decode" if fq.auto_path(M, N, K) == fq.PATH_DECODE else "prefill",
+            "tile": (None if fq.auto_path(M, N, K) == fq.PATH_DECODE else
+                     TILE_NAMES[fq.prefill_tile(M, N, K)]),
             "gemm_us": round(g * 1e3, 2), "quant_us": round(q * 1e3, 2),
             "tops": round(ops / (g * 1e-3) / 1e12, 2),
             "gbs": round(by / (g * 1e-3) / 1e9, 1),

@@ -74,7 +74,13 @@ typedef enum {
 typedef enum {
   FLEXQ_PATH_AUTO = 0,    /* see flexq_gemm_w6ax_auto_path */
   FLEXQ_PATH_DECODE = 1,  /* HBM-streaming kernel for few tokens (any M is accepted) */
-  FLEXQ_PATH_PREFILL = 2  /* MFMA-bound tiled kernel for many tokens (any M is accepted) */
+  FLEXQ_PATH_PREFILL = 2, /* MFMA-bound tiled kernel for many tokens (any M is accepted),
+                             tile chosen as flexq_gemm_w6ax_prefill_tile reports */
+  /* the prefill kernel with a fixed workgroup tile (rows x columns), for tests and
+     tuning; every tile accepts every shape and gives the same bits */
+  FLEXQ_PATH_PREFILL_256X128 = 3,
+  FLEXQ_PATH_PREFILL_128X128 = 4,
+  FLEXQ_PATH_PREFILL_128X64 = 5
 } flexq_path;
 
 #define FLEXQ_ABI_VERSION 1
@@ -132,8 +138,16 @@ flexq_status flexq_gemm_w6ax(const int8_t* q_a, const float* s_a, const uint32_t
    enter the choice.  Never fails (M <= 0 or N <= 0 report FLEXQ_PATH_DECODE). */
 int flexq_gemm_w6ax_auto_path(int64_t M, int64_t N, int64_t K);
 
-/* flexq_gemm_w6ax with an explicit kernel choice (flexq_path); both kernels accept
-   every M and give identical results. */
+/* The tile FLEXQ_PATH_PREFILL uses for an M x N x K product on the current device
+   (one of FLEXQ_PATH_PREFILL_256X128 / _128X128 / _128X64): the 256 x 128 tile when
+   the grid of 128 x 128 tiles needs enough more rounds of one tile per compute unit
+   (rounds256 * 1.46 < rounds128), else 128 x 64 when 128 x 128 tiles would number
+   no more than the compute units, else 128 x 128.  K does not enter the choice.
+   Never fails. */
+int flexq_gemm_w6ax_prefill_tile(int64_t M, int64_t N, int64_t K);
+
+/* flexq_gemm_w6ax with an explicit kernel choice (flexq_path); every kernel and
+   tile accepts every M and gives identical results. */
 flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a,
                                   const uint32_t* w_packed, const uint16_t* s_w_fp16,
                                   int64_t M, int64_t N, int64_t K, int32_t group_size,

@@ -199,3 +199,31 @@ def test_auto_path_rule(flexq):
     assert fq.auto_path(65, 16, 128) == PRE
     assert fq.auto_path(4096, 16, 128) == PRE
     assert fq.auto_path(0, 128, 128) == DEC
+
+
+def test_prefill_tile_rule(flexq):
+    """The prefill tile choice as flexq.h states it (256 CUs without a GPU)."""
+    import w6a6_w6a8_integer_amd as fq
+    T256, T128, T64 = fq.PATH_PREFILL_256X128, fq.PATH_PREFILL_128X128, fq.PATH_PREFILL_128X64
+    # LLaMA-2-70B layers
+    assert fq.prefill_tile(4096, 57344, 8192) == T256    # 7168 vs 14336 tiles
+    assert fq.prefill_tile(1024, 8192, 8192) == T256     # 1 round vs 2
+    assert fq.prefill_tile(1024, 10240, 8192) == T256    # 2 rounds vs 3: 2.92 < 3
+    assert fq.prefill_tile(256, 8192, 28672) == T64      # 128 tiles of 128 x 128 <= 256
+    assert fq.prefill_tile(256, 10240, 8192) == T64      # 160 <= 256
+    assert fq.prefill_tile(512, 8192, 8192) == T64       # 256 <= 256: one round either way
+    assert fq.prefill_tile(512, 10240, 8192) == T256     # 1 round vs 2
+    assert fq.prefill_tile(256, 57344, 8192) == T256     # 2 rounds vs 4
+    assert fq.prefill_tile(64, 57344, 8192) == T128      # 448 tiles: 2 rounds either way
+    # the boundary between the narrow and the square tile
+    assert fq.prefill_tile(128, 32768, 256) == T64       # 256 tiles of 128 x 128
+    assert fq.prefill_tile(128, 32784, 256) == T128      # 257
+    assert fq.prefill_tile(0, 16, 128) == T64
+
+
+def test_gemm_path_values(flexq):
+    f = flexq.flexq_gemm_w6ax_path
+    for bad in (-1, 6, 7):
+        assert f(A16, 2 * A16, 3 * A16, 4 * A16, 4, 16, 128, 128, 6, bad, 5 * A16, None) == INVALID
+    for p in range(6):  # every valid path with M = 0: a no-op
+        assert f(None, None, 3 * A16, 4 * A16, 0, 16, 128, 128, 6, p, None, None) == SUCCESS

@@ -4,6 +4,7 @@ Bit-exact everywhere: packed weights, weight scales, activation codes and scales
 int32 group dots, and Y (both GEMM kernels keep the sequential ascending-group
 fp32 order of the definition, so Y matches to the last bit).
 """
+import functools
 import os
 
 import numpy as np
@@ -186,11 +187,16 @@ def test_group_dots_extreme_codes(fq):
 # GEMM: both kernels, many shapes, bit-exact Y
 # ---------------------------------------------------------------------------
 
-def run_gemm_case(fq, M, N, K, abits, path, seed=4):
+@functools.lru_cache(maxsize=4)
+def oracle_gemm_case(M, N, K, abits, seed):
     x, w = inputs(seed, M, N, K)
     qa, sa = oracle.quant_act(x, abits)
     wp, sw = oracle.pack_w6(w)
-    y_ref = oracle.gemm_packed(qa, sa, wp, sw, N)
+    return qa, sa, wp, sw, oracle.gemm_packed(qa, sa, wp, sw, N)
+
+
+def run_gemm_case(fq, M, N, K, abits, path, seed=4):
+    qa, sa, wp, sw, y_ref = oracle_gemm_case(M, N, K, abits, seed)
     y = fq.gemm_w6ax(to_dev(qa), to_dev(gm(sa)), to_dev(wp.view(np.int32)), to_dev(gm(sw)), N,
                      abits, path=path)
     got = u16(y)
@@ -202,7 +208,9 @@ def run_gemm_case(fq, M, N, K, abits, path, seed=4):
 # half-empty last pair, and give each workgroup 2 to 5 work items, so the items of a
 # workgroup share their activation fragments in chunks of 2, 4 and 8; with 300 rows
 # the chunks are also cut where a workgroup's items cross into the next 64-row pass.
-# The last two run the prefill kernel's 128- and 256-row tiles on wide N.)
+# Every shape also runs each prefill tile (256 x 128, 128 x 128, 128 x 64) by name,
+# on ragged row and column counts; the last two take the 256-row tile by the
+# automatic choice.)
 SHAPES = [(16, 256, 512), (1, 16, 128), (5, 48, 1152), (17, 272, 640), (33, 160, 384),
           (64, 128, 2048), (65, 144, 512), (128, 256, 1024), (130, 400, 768), (257, 96, 256),
           (300, 528, 1280), (1024, 256, 512), (1100, 400, 384), (2048, 128, 1024),
@@ -210,9 +218,10 @@ SHAPES = [(16, 256, 512), (1, 16, 128), (5, 48, 1152), (17, 272, 640), (33, 160,
           (300, 16368, 256), (256, 16384, 256), (1024, 8192, 256)]
 
 
+@pytest.mark.parametrize("path", [1, 2, 3, 4, 5],
+                         ids=["decode", "prefill", "tile256x128", "tile128x128", "tile128x64"])
 @pytest.mark.parametrize("M,N,K", SHAPES)
-@pytest.mark.parametrize("path", [1, 2], ids=["decode", "prefill"])
-def test_gemm_bit_exact_both_paths(fq, M, N, K, path):
+def test_gemm_bit_exact_every_path(fq, M, N, K, path):
     say(f"gemm M={M} N={N} K={K} path={path}")
     run_gemm_case(fq, M, N, K, 6 if (M + N) % 2 else 8, path)
 
@@ -230,7 +239,7 @@ def test_gemm_zero_rows_and_zero_groups(fq):
     x[5, G:2 * G] = 0
     w[7] = 0
     w[9, :G] = 0
-    for path in (1, 2):
+    for path in (1, 3, 4, 5):   # decode, then each prefill tile
         qa, sa = oracle.quant_act(x, 6)
         wp, sw = oracle.pack_w6(w)
         y_ref = oracle.gemm_packed(qa, sa, wp, sw, N)
@@ -247,7 +256,7 @@ def test_gemm_deterministic_and_in_bounds(fq):
     qa, sa = oracle.quant_act(x, 8)
     wp, sw = oracle.pack_w6(w)
     args = (to_dev(qa), to_dev(gm(sa)), to_dev(wp.view(np.int32)), to_dev(gm(sw)))
-    for path in (1, 2):
+    for path in (1, 3, 4, 5):   # decode, then each prefill tile
         buf = torch.full((M * N + 4096,), -1, dtype=torch.int16, device=DEV)
         y = buf[:M * N].view(torch.float16).view(M, N)
         fq.gemm_w6ax(*args, N, 8, y=y, path=path)
@@ -268,7 +277,7 @@ def test_gemm_output_not_16_byte_aligned(fq, M, N, K):
     wp, sw = oracle.pack_w6(w)
     y_ref = oracle.gemm_packed(qa, sa, wp, sw, N).view(np.uint16)
     args = (to_dev(qa), to_dev(gm(sa)), to_dev(wp.view(np.int32)), to_dev(gm(sw)))
-    for path in (1, 2):
+    for path in (1, 3, 4, 5):   # decode, then each prefill tile
         buf = torch.full((M * N + 4096,), -1, dtype=torch.int16, device=DEV)
         y = buf[2:2 + M * N].view(torch.float16).view(M, N)   # 4 bytes past a 16-byte boundary
         assert y.data_ptr() % 16 == 4

@@ -28,6 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libflexq.so")
 GROUP = 128
 DECODE_MAX_M = 64
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+# the prefill kernel with a fixed workgroup tile (rows x columns)
+PATH_PREFILL_256X128, PATH_PREFILL_128X128, PATH_PREFILL_128X64 = 3, 4, 5
 
 STATUS_NAMES = {0: "FLEXQ_SUCCESS", 1: "FLEXQ_ERROR_INVALID_VALUE", 2: "FLEXQ_ERROR_UNSUPPORTED",
                 3: "FLEXQ_ERROR_LAUNCH"}
@@ -45,6 +47,7 @@ SIGNATURES = {
                                             _P, _P]),
     "flexq_gemm_w6ax_group_dots": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _P, _P]),
     "flexq_gemm_w6ax_auto_path": (ctypes.c_int, [_I64, _I64, _I64]),
+    "flexq_gemm_w6ax_prefill_tile": (ctypes.c_int, [_I64, _I64, _I64]),
     "flexq_linear_w6ax_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "flexq_linear_w6ax": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P,
                                          ctypes.c_size_t, _P, _P]),
@@ -181,6 +184,12 @@ def gemm_w6ax_group_dots(q_a: torch.Tensor, w_packed: torch.Tensor, N: int,
                                             dots.data_ptr(), _stream(q_a)),
            "flexq_gemm_w6ax_group_dots")
     return dots
+
+
+def prefill_tile(M: int, N: int, K: int) -> int:
+    """PATH_PREFILL_256X128 / _128X128 / _128X64: the tile PATH_PREFILL uses for this
+    shape on the current device (flexq_gemm_w6ax_prefill_tile)."""
+    return int(lib().flexq_gemm_w6ax_prefill_tile(M, N, K))
 
 
 def auto_path(M: int, N: int, K: int) -> int:

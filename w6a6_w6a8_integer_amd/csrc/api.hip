@@ -148,8 +148,7 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a, const uin
   FLEXQ_TRY(check_scales(M, K));
   FLEXQ_TRY(check_scales(N, K));
   if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
-  if (path != FLEXQ_PATH_AUTO && path != FLEXQ_PATH_DECODE && path != FLEXQ_PATH_PREFILL)
-    return FLEXQ_ERROR_INVALID_VALUE;
+  if (path < FLEXQ_PATH_AUTO || path > FLEXQ_PATH_PREFILL_128X64) return FLEXQ_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return FLEXQ_SUCCESS;
   FLEXQ_TRY(validate_gemm_operands(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16,
                                    (uint64_t)M * N * 2));
@@ -157,7 +156,21 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a, const uin
   hipStream_t s = (hipStream_t)stream;
   if (path == FLEXQ_PATH_DECODE)
     return launched(flexq::launch_gemm_decode(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
-  return launched(flexq::launch_gemm_prefill(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
+  const int tile = path == FLEXQ_PATH_PREFILL_256X128   ? flexq::kTile256x128
+                   : path == FLEXQ_PATH_PREFILL_128X128 ? flexq::kTile128x128
+                   : path == FLEXQ_PATH_PREFILL_128X64  ? flexq::kTile128x64
+                                                        : flexq::kTileAuto;
+  return launched(
+      flexq::launch_gemm_prefill(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s, tile));
+}
+
+int flexq_gemm_w6ax_prefill_tile(int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  if (M <= 0 || N <= 0) return FLEXQ_PATH_PREFILL_128X64;
+  const int t = flexq::prefill_tile(M, N);
+  return t == flexq::kTile256x128   ? FLEXQ_PATH_PREFILL_256X128
+         : t == flexq::kTile128x128 ? FLEXQ_PATH_PREFILL_128X128
+                                    : FLEXQ_PATH_PREFILL_128X64;
 }
 
 int flexq_gemm_w6ax_auto_path(int64_t M, int64_t N, int64_t K) {

@@ -15,11 +15,12 @@
 //
 // So every output is bit-identical to the sequential definition.
 //
-// Tile: BM x 128 per workgroup (BM = 256 or 128, whichever finishes the grid in
-// less time), BM/32 waves, each wave 64 x 64 outputs = 2 x 2 MFMA tiles of
-// 32 x 32, handled as two row tiles.  A group is written out as 16 steps of one MFMA each: the 8 steps of row
-// tile 0 overlap the rescale of the previous group's row tile 1, the 8 steps of row
-// tile 1 the rescale of this group's row tile 0 and the unpack of the next group.
+// Tile: BM x BN per workgroup (256 x 128, 128 x 128 or 128 x 64, see prefill_tile),
+// BM/32 waves, each wave 64 x 32*TN outputs = 2 x TN MFMA tiles of 32 x 32 (TN = 2,
+// or 1 for the 64-wide tile), handled as two row tiles.  A group is written out as
+// 8*TN steps of one MFMA each: the 4*TN steps of row tile 0 overlap the rescale of
+// the previous group's row tile 1, the 4*TN steps of row tile 1 the rescale of this
+// group's row tile 0 and the unpack of the next group.
 // The 16 activation scales a lane needs for one 32 x 32 tile arrive in one register
 // (lane 16j + r holds the scale of output register r) and the accumulate is a
 // v_fmac_f32 with DPP row_newbcast:r, which hands lane r of each 16-lane row to
@@ -58,7 +59,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int BN = 128;
 constexpr int STAGES = 3;
 constexpr int kOutPitch = 144;
 // which scale vector a wave loads in the main loop
@@ -103,11 +103,13 @@ __device__ __forceinline__ void rescale4(float (&a)[16], const f32x16& F, float 
 
 }  // namespace
 
-template <int BM>
+template <int BM, int BN>
 struct PrefillCfg {
   static constexpr int THREADS = BM * 2;
   static constexpr int WAVES = THREADS / 64;
-  static constexpr int RB = BM / 32;                 // 32-row blocks
+  static constexpr int WM = BM / 64;                 // waves along M (64 rows each)
+  static constexpr int WN = WAVES / WM;              // waves along N
+  static constexpr int TN = BN / WN / 32;            // 32-column MFMA tiles per wave
   static constexpr int A_BYTES = BM * kGroup;        // activation stage
   static constexpr int B_BYTES = BN * kGroup;        // unpacked weight stage
   static constexpr int A_BLOCKS = A_BYTES / 1024;    // 1 KB fragment blocks
@@ -119,11 +121,14 @@ struct PrefillCfg {
   static constexpr int DMA_OPS = A_BLOCKS_PER_WAVE + 1;
 };
 
-template <int BM>
+template <int BM, int BN>
 __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint32_t* __restrict__ wp,
     const uint16_t* __restrict__ sw, int M, int N, int K, int GM, uint16_t* __restrict__ y) {
-  using C = PrefillCfg<BM>;
+  using C = PrefillCfg<BM, BN>;
+  constexpr int TN = C::TN;
+  static_assert(TN == 1 || TN == 2, "one or two 32-column tiles per wave");
+  static_assert(C::WN * TN * 32 == BN, "waves cover the tile's columns");
   static_assert(C::A_BLOCKS_PER_WAVE == 4, "tile/thread mismatch");
   static_assert(C::WAVES * 64 * kOutPitch <= STAGES * C::STAGE_BYTES, "output staging fits");
   static_assert(C::B_UNITS * C::THREADS == BN * 8, "B split");
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % (BM / 64), wn = wave / (BM / 64);
+  const int wm = wave % C::WM, wn = wave / C::WM;
 
   // ---- logical tile from the workgroup id (XCD-contiguous, row-band order)
   const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
@@ -187,8 +192,10 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // (1536 contiguous bytes per tile and group, unit slot j = u_local*16 + n%16).
   // Load i of a lane takes slot (i%2)*64 + lane of tile TPW*w + i/2, so every load
   // instruction reads 768 contiguous bytes; in fragment order that unit lands at
-  // b_lds0 + (i%2)*8192 + ((i/2)%2)*256 + (i/4)*1024 (TPW*w is a multiple of TPW).
+  // b_lds0 + (i%2)*2*KC_BYTES + ((i/2)%2)*256 + (i/4)*1024 (TPW*w is a multiple of
+  // TPW; KC_BYTES is one 32-deep k-chunk of the B stage).
   constexpr int TPW = (BN / 16) / C::WAVES;
+  constexpr int KC_BYTES = (BN / 32) * 1024;
   static_assert(C::B_UNITS == 2 * TPW && (TPW == 1 || TPW == 2 || TPW == 4), "B load split");
   const int b_tile0 = wave * TPW;
   const uint32_t b_voff = (uint32_t)b_tile0 * 12u * (uint32_t)K + (uint32_t)lane * 12u;
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   };
   // Unpack unit i of a register set, and its weight scale, into the stage at `so`.
   auto fill_unit = [&](int so, const BRegs& r, int i) {
-    *reinterpret_cast<i32x4*>(lds + so + C::A_BYTES + b_lds0 + (i & 1) * 8192 +
+    *reinterpret_cast<i32x4*>(lds + so + C::A_BYTES + b_lds0 + (i & 1) * 2 * KC_BYTES +
                               ((i >> 1) & 1) * 256 + (i >> 2) * 1024) =
         unpack_unit_x4(r.u[i][0], r.u[i][1], r.u[i][2]);
   };
@@ -277,12 +284,13 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     }
   };
   static_assert(C::DMA_OPS == 5, "vmem_op numbering");
+  static_assert(OPS_PER_GROUP <= 8 * C::TN, "one vector-memory instruction per MFMA step");
 
-  float acc[2][2][16];
+  float acc[2][TN][16];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < TN; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
@@ -293,10 +301,15 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // Deferred row tile 1 of the previous group: MFMA results, its packed s_a
   // register and s_w / 4.  The starting values make the first deferred rescale add
   // exactly +0 (t = fma(F0, 0, -0) = +0, then acc + S * t with S = 0).
-  i32x16 dprev[2] = {magic, magic};
+  i32x16 dprev[TN];
+  float s4prev[TN], bprev[TN];  // bprev = -12582912 * s4prev
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    dprev[tn] = magic;
+    s4prev[tn] = 0.0f;
+    bprev[tn] = -0.0f;
+  }
   float Sprev = 0.0f;
-  float s4prev[2] = {0.0f, 0.0f};
-  float bprev[2] = {-0.0f, -0.0f};  // -12582912 * s4prev
 
   // per-lane byte offsets inside a stage
   const int r32 = lane & 31, hl = lane >> 5;
@@ -304,19 +317,19 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
 #pragma unroll
   for (int c = 0; c < 4; ++c)
     a_off[c] = (wm * 64 + r32) * 128 + (((2 * c + hl) ^ ((r32 >> 1) & 7)) * 16);
-  // B fragment (c, tn): block c * (BN / 32) + wn * 2 + tn, lane-linear
-  const int b_off = C::A_BYTES + wn * 2048 + lane * 16;
+  // B fragment (c, tn): block c * (BN / 32) + wn * TN + tn, lane-linear
+  const int b_off = C::A_BYTES + wn * TN * 1024 + lane * 16;
   // s_a row held by this lane in the packed scale register of row tile tm (+128 * tm)
   const int sa_off =
       C::A_BYTES + C::B_BYTES + (wm * 64 + 8 * ((lane >> 2) & 3) + 4 * hl + (lane & 3)) * 4;
   // s_w / 4 of this lane's column in column tile tn (+128 * tn)
-  const int s4_off = C::A_BYTES + C::B_BYTES + BM * 4 + (wn * 64 + r32) * 4;
+  const int s4_off = C::A_BYTES + C::B_BYTES + BM * 4 + (wn * TN * 32 + r32) * 4;
 
   auto ldA = [&](int so, int c, int tm) {
     return *reinterpret_cast<const i32x4*>(lds + so + a_off[c] + tm * 4096);
   };
   auto ldB = [&](int so, int c, int tn) {
-    return *reinterpret_cast<const i32x4*>(lds + so + b_off + c * 4096 + tn * 1024);
+    return *reinterpret_cast<const i32x4*>(lds + so + b_off + c * KC_BYTES + tn * 1024);
   };
   auto ldS = [&](int so, int tm) {
     return *reinterpret_cast<const float*>(lds + so + sa_off + tm * 128);
@@ -338,10 +351,10 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   barrier();
 
-  // One group g in stage `so`, written as 16 steps of one MFMA each.  The first
-  // eight (row tile 0) overlap the rescale of the previous group's row tile 1, the
-  // last eight (row tile 1) the rescale of this group's row tile 0 and the unpack
-  // of group g+1.  LDS reads run two or more steps ahead of their MFMA; the B
+  // One group g in stage `so`, written as 8*TN steps of one MFMA each.  The first
+  // 4*TN (row tile 0) overlap the rescale of the previous group's row tile 1, the
+  // last 4*TN (row tile 1) the rescale of this group's row tile 0 and the unpack of
+  // group g+1.  LDS reads run two or more steps ahead of their MFMA; the B
   // fragments stay in registers for both row tiles.  `mine` held group g and now
   // receives group g+2; `other` holds group g+1.
   auto step_group = [&](auto role, int g, int so, int so_next, int so_dma, BRegs& mine,
@@ -350,91 +363,103 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     // group g-1 used, one vector-memory instruction per MFMA step
     const int gn = min(g + 2, glast);
 
-    i32x4 a0[4], a1[4], b[4][2];
-    i32x16 d0[2], d1[2];
-    float S0, S1, s4c[2];
-    const f32x16 Fp0 = __builtin_bit_cast(f32x16, dprev[0]);
-    const f32x16 Fp1 = __builtin_bit_cast(f32x16, dprev[1]);
-    const float bp0 = bprev[0], bp1 = bprev[1];
+    i32x4 a0[4], a1[4], b[4][TN];
+    i32x16 d0[TN], d1[TN];
+    float S0, S1, s4c[TN], bc[TN];
+    f32x16 Fp[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) Fp[tn] = __builtin_bit_cast(f32x16, dprev[tn]);
     const float Sp = Sprev;
 
+    // LDS reads of this stage, each at least two steps before its MFMA: k-chunks 0
+    // and 1 up front, the rest spread over row tile 0 (schedule per tile width).
     a0[0] = ldA(so, 0, 0);
-    b[0][0] = ldB(so, 0, 0);
-    b[0][1] = ldB(so, 0, 1);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) b[0][tn] = ldB(so, 0, tn);
     a0[1] = ldA(so, 1, 0);
-    b[1][0] = ldB(so, 1, 0);
-    b[1][1] = ldB(so, 1, 1);
-    rescale4<0>(acc[1][0], Fp0, s4prev[0], bp0, Sp);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) b[1][tn] = ldB(so, 1, tn);
+    rescale4<0>(acc[1][0], Fp[0], s4prev[0], bprev[0], Sp);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- row tile 0
+    // ---- row tile 0: 4 * TN steps (k-chunk c = k / TN, column tile tn = k % TN)
+    constexpr int STEPS = 4 * TN;
+    static_assert(STEPS <= OPS_PER_GROUP, "row tile 0 issues only real loads");
     unroll([&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      constexpr int c = k >> 1, tn = k & 1;
+      constexpr int c = k / TN, tn = k % TN;
       vmem_op(role, kc, gn, so_dma, mine);
-      if constexpr (k == 0) a0[2] = ldA(so, 2, 0);
-      if constexpr (k == 1) b[2][0] = ldB(so, 2, 0);
-      if constexpr (k == 2) b[2][1] = ldB(so, 2, 1);
-      if constexpr (k == 3) a0[3] = ldA(so, 3, 0);
-      if constexpr (k == 4) b[3][0] = ldB(so, 3, 0);
-      if constexpr (k == 5) b[3][1] = ldB(so, 3, 1);
-      if constexpr (k == 6) {
+      if constexpr (TN == 2) {
+        if constexpr (k == 0) a0[2] = ldA(so, 2, 0);
+        if constexpr (k == 1) b[2][0] = ldB(so, 2, 0);
+        if constexpr (k == 2) b[2][TN - 1] = ldB(so, 2, TN - 1);
+        if constexpr (k == 3) a0[3] = ldA(so, 3, 0);
+        if constexpr (k == 4) b[3][0] = ldB(so, 3, 0);
+        if constexpr (k == 5) b[3][TN - 1] = ldB(so, 3, TN - 1);
+      } else {
+        if constexpr (k == 0) {
+          a0[2] = ldA(so, 2, 0);
+          b[2][0] = ldB(so, 2, 0);
+        }
+        if constexpr (k == 1) {
+          a0[3] = ldA(so, 3, 0);
+          b[3][0] = ldB(so, 3, 0);
+        }
+      }
+      if constexpr (k == STEPS - 2) {
         a1[0] = ldA(so, 0, 1);
         S0 = ldS(so, 0);
-        s4c[0] = ldS4(so, 0);
-        s4c[1] = ldS4(so, 1);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) s4c[t] = ldS4(so, t);
       }
-      if constexpr (k == 7) {
+      if constexpr (k == STEPS - 1) {
         a1[1] = ldA(so, 1, 1);
         S1 = ldS(so, 1);
       }
       d0[tn] = mfma32(a0[c], b[c][tn], c == 0 ? magic : d0[tn]);
-      // outputs 4 .. 31 of the deferred tile, four per step
-      if constexpr (k < 7) {
+      // outputs 4 .. 16 * TN - 1 of the deferred tile, four per step
+      if constexpr (k < STEPS - 1) {
         constexpr int o = 4 * (k + 1);
-        if constexpr (o < 16)
-          rescale4<o>(acc[1][0], Fp0, s4prev[0], bp0, Sp);
-        else
-          rescale4<o - 16>(acc[1][1], Fp1, s4prev[1], bp1, Sp);
+        rescale4<o % 16>(acc[1][o / 16], Fp[o / 16], s4prev[o / 16], bprev[o / 16], Sp);
       }
       __builtin_amdgcn_sched_barrier(0);
-    }, std::make_integer_sequence<int, 8>{});
+    }, std::make_integer_sequence<int, STEPS>{});
 
     // ---- row tile 1
-    const f32x16 F00 = __builtin_bit_cast(f32x16, d0[0]);
-    const f32x16 F01 = __builtin_bit_cast(f32x16, d0[1]);
-    const float bc0 = -kMagicF * s4c[0], bc1 = -kMagicF * s4c[1];
+    f32x16 F0[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      F0[tn] = __builtin_bit_cast(f32x16, d0[tn]);
+      bc[tn] = -kMagicF * s4c[tn];
+    }
     unroll([&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      constexpr int c = k >> 1, tn = k & 1;
-      if constexpr (8 + k < OPS_PER_GROUP)
-        vmem_op(role, std::integral_constant<int, 8 + k>{}, gn, so_dma, mine);
+      constexpr int c = k / TN, tn = k % TN;
+      if constexpr (STEPS + k < OPS_PER_GROUP)
+        vmem_op(role, std::integral_constant<int, STEPS + k>{}, gn, so_dma, mine);
       if constexpr (k == 0) a1[2] = ldA(so, 2, 1);
       if constexpr (k == 1) a1[3] = ldA(so, 3, 1);
       d1[tn] = mfma32(a1[c], b[c][tn], c == 0 ? magic : d1[tn]);
-      if constexpr (k < 4)
-        rescale4<4 * k>(acc[0][0], F00, s4c[0], bc0, S0);
-      else
-        rescale4<4 * (k - 4)>(acc[0][1], F01, s4c[1], bc1, S0);
-      // the unpack of group g+1: unit u at step 1 + 6u/B_UNITS, then its scale
+      rescale4<4 * (k % 4)>(acc[0][k / 4], F0[k / 4], s4c[k / 4], bc[k / 4], S0);
+      // the unpack of group g+1: unit u at step 1 + (STEPS - 2)u/B_UNITS, then its scale
       unroll([&](auto uc) {
         constexpr int u = decltype(uc)::value;
-        if constexpr (k == 1 + (u * 6) / C::B_UNITS) fill_unit(so_next, other, u);
+        if constexpr (k == 1 + (u * (STEPS - 2)) / C::B_UNITS) fill_unit(so_next, other, u);
       }, std::make_integer_sequence<int, C::B_UNITS>{});
-      if constexpr (k == 7) {
+      if constexpr (k == STEPS - 1) {
         if constexpr (decltype(role)::value == kRoleSw) fill_scale(so_next, other);
       }
       __builtin_amdgcn_sched_barrier(0);
-    }, std::make_integer_sequence<int, 8>{});
+    }, std::make_integer_sequence<int, STEPS>{});
 
     // row tile 1 is rescaled during the next group's row tile 0
-    dprev[0] = d1[0];
-    dprev[1] = d1[1];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      dprev[tn] = d1[tn];
+      s4prev[tn] = s4c[tn];
+      bprev[tn] = bc[tn];
+    }
     Sprev = S1;
-    s4prev[0] = s4c[0];
-    s4prev[1] = s4c[1];
-    bprev[0] = bc0;
-    bprev[1] = bc1;
 
     // everything issued before this group's loads has landed (group g+1's DMA), and
     // this group's fills and LDS reads are done before anyone passes the barrier.
@@ -471,20 +496,18 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   else
     main_loop(std::integral_constant<int, kRoleNone>{});
   wait_vm_lgkm0<0>();  // no copy into LDS may outlive the workgroup
-  {
-    const f32x16 Fp0 = __builtin_bit_cast(f32x16, dprev[0]);
-    const f32x16 Fp1 = __builtin_bit_cast(f32x16, dprev[1]);
-    const float bp0 = bprev[0], bp1 = bprev[1];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const f32x16 Fp = __builtin_bit_cast(f32x16, dprev[tn]);
     unroll([&](auto kc) {
       constexpr int q = decltype(kc)::value;
-      rescale4<4 * q>(acc[1][0], Fp0, s4prev[0], bp0, Sprev);
-      rescale4<4 * q>(acc[1][1], Fp1, s4prev[1], bp1, Sprev);
+      rescale4<4 * q>(acc[1][tn], Fp, s4prev[tn], bprev[tn], Sprev);
     }, std::make_integer_sequence<int, 4>{});
   }
 
-  // Epilogue.  With a 16-byte aligned Y, each wave stages its 64 x 64 fp16 outputs
+  // Epilogue.  With a 16-byte aligned Y, each wave stages its 64 x 32TN fp16 outputs
   // in LDS (its own region, row pitch kOutPitch) and stores every row as 16-byte
-  // chunks: 8 store instructions per lane instead of 64 two-byte ones.  The barrier
+  // chunks: 4TN store instructions per lane instead of 32TN two-byte ones.  The barrier
   // lets no wave overwrite a stage while another wave's copies into it may still
   // land.  (N is a multiple of 16, so an 8-column chunk is wholly inside or outside
   // the matrix and every row starts 16-byte aligned.)
@@ -494,7 +517,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn)
+      for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int lr = tm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -502,11 +525,12 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
               float_to_half_bits(acc[tm][tn][r]);
         }
     __builtin_amdgcn_wave_barrier();
-    const int col = wn * 64 + (lane & 7) * 8;
+    constexpr int CH = 4 * TN;  // 16-byte chunks per staged row
+    const int col = wn * TN * 32 + (lane % CH) * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int lr = i * 8 + (lane >> 3);
-      const i32x4 v = *reinterpret_cast<const i32x4*>(tw + lr * kOutPitch + (lane & 7) * 16);
+    for (int i = 0; i < CH; ++i) {
+      const int lr = i * (64 / CH) + lane / CH;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(tw + lr * kOutPitch + (lane % CH) * 16);
       const int row = wm * 64 + lr;
       if (row < mrows && col < ncols)
         *reinterpret_cast<i32x4*>(y + (size_t)(m0 + row) * N + n0 + col) = v;
@@ -517,8 +541,8 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
 #pragma unroll
   for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) {
-      const int col = wn * 64 + tn * 32 + (lane & 31);
+    for (int tn = 0; tn < TN; ++tn) {
+      const int col = wn * TN * 32 + tn * 32 + (lane & 31);
       if (col < ncols) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -530,31 +554,51 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     }
 }
 
-template <int BM>
+template <int BM, int BN>
 static void launch_prefill_t(const int8_t* qa, const float* sa, const uint32_t* wp,
                              const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                              hipStream_t stream) {
   const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   const int GM = 4;
-  hipLaunchKernelGGL(gemm_prefill_kernel<BM>, dim3((unsigned)(nbm * nbn)), dim3(BM * 2), 0,
+  hipLaunchKernelGGL((gemm_prefill_kernel<BM, BN>), dim3((unsigned)(nbm * nbn)), dim3(BM * 2), 0,
                      stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, GM, y);
+}
+
+int prefill_tile(int64_t M, int64_t N) {
+  // The grid runs in rounds of one 256- or 128-row tile per CU (their LDS rings
+  // allow no second one); a round of 256 x 128 tiles takes about 1.46 times as long
+  // as a round of 128 x 128 tiles (83 vs 57 us at K = 8192 on the LLaMA-2-70B
+  // shapes), so the taller, more efficient tile is taken when it needs enough fewer
+  // rounds.  When even the 128 x 128 grid leaves CUs idle (at most one tile per
+  // CU), 128 x 64 tiles double the grid: one of them takes about 0.7 of a 128 x 128
+  // round, two share a CU (half-size ring) in about 1.0 (LLaMA-2-70B layers at
+  // M = 64 ... 512: 25-30 % faster on o and down).
+  const int64_t cu = device_cu_count();
+  const int64_t nbn = (N + 127) / 128;
+  const int64_t tiles128 = (M + 127) / 128 * nbn;
+  const int64_t rounds256 = ((M + 255) / 256 * nbn + cu - 1) / cu;
+  const int64_t rounds128 = (tiles128 + cu - 1) / cu;
+  if (rounds256 * 146 < rounds128 * 100) return kTile256x128;
+  return tiles128 <= cu ? kTile128x64 : kTile128x128;
 }
 
 hipError_t launch_gemm_prefill(const int8_t* qa, const float* sa, const uint32_t* wp,
                                const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
-                               hipStream_t stream) {
-  // Tile height: the grid runs in rounds of one workgroup per CU, and a round of
-  // 256-row tiles takes about 1.46 times as long as a round of 128-row tiles
-  // (83 vs 57 us per round at K = 8192 on the LLaMA-2-70B shapes), so the taller,
-  // more efficient tile is taken when it needs enough fewer rounds.
-  const int64_t cu = device_cu_count();
-  const int64_t nbn = (N + BN - 1) / BN;
-  const int64_t rounds256 = ((M + 255) / 256 * nbn + cu - 1) / cu;
-  const int64_t rounds128 = ((M + 127) / 128 * nbn + cu - 1) / cu;
-  if (rounds256 * 146 < rounds128 * 100)
-    launch_prefill_t<256>(qa, sa, wp, sw, M, N, K, y, stream);
-  else
-    launch_prefill_t<128>(qa, sa, wp, sw, M, N, K, y, stream);
+                               hipStream_t stream, int tile) {
+  if (tile == kTileAuto) tile = prefill_tile(M, N);
+  switch (tile) {
+    case kTile256x128:
+      launch_prefill_t<256, 128>(qa, sa, wp, sw, M, N, K, y, stream);
+      break;
+    case kTile128x128:
+      launch_prefill_t<128, 128>(qa, sa, wp, sw, M, N, K, y, stream);
+      break;
+    case kTile128x64:
+      launch_prefill_t<128, 64>(qa, sa, wp, sw, M, N, K, y, stream);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

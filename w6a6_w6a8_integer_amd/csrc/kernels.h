@@ -16,9 +16,15 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
                               const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                               hipStream_t stream);
 
+// Prefill tile shapes (rows x columns per workgroup); kTileAuto = prefill_tile(M, N).
+constexpr int kTileAuto = 0, kTile256x128 = 1, kTile128x128 = 2, kTile128x64 = 3;
+
+// The tile the prefill kernel uses for an M x N product on the current device.
+int prefill_tile(int64_t M, int64_t N);
+
 hipError_t launch_gemm_prefill(const int8_t* qa, const float* sa, const uint32_t* wp,
                                const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
-                               hipStream_t stream);
+                               hipStream_t stream, int tile = kTileAuto);
 
 hipError_t launch_group_dots(const int8_t* qa, const uint32_t* wp, int64_t M, int64_t N,
                              int64_t K, int32_t* dots, hipStream_t stream);
