@@ -132,7 +132,7 @@ flexq_status flexq_gemm_w6ax(const int8_t* q_a, const float* s_a, const uint32_t
                              int32_t group_size, int32_t abits, uint16_t* y_fp16, void* stream);
 
 /* The kernel FLEXQ_PATH_AUTO runs for an M x N x K product on the current device:
-   FLEXQ_PATH_DECODE (the weight-streaming kernel) for M <= 32, and for
+   FLEXQ_PATH_DECODE (the weight-streaming kernel) for M <= 48, and for
    M <= FLEXQ_DECODE_MAX_M when the prefill kernel's 128 x 128 tiles would number
    fewer than the device's compute units; FLEXQ_PATH_PREFILL otherwise.  K does not
    enter the choice.  Never fails (M <= 0 or N <= 0 report FLEXQ_PATH_DECODE). */

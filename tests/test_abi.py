@@ -184,12 +184,14 @@ def test_binding_refuses_cpu_tensors():
 
 def test_auto_path_rule(flexq):
     """The automatic kernel choice as flexq.h states it (with no GPU the CU count
-    falls back to MI355X's 256): decode up to 32 rows, decode up to 64 rows when the
+    falls back to MI355X's 256): decode up to 48 rows, decode up to 64 rows when the
     128-wide prefill tiles would not cover the CUs, prefill otherwise."""
     import w6a6_w6a8_integer_amd as fq
     DEC, PRE = fq.PATH_DECODE, fq.PATH_PREFILL
     assert fq.auto_path(1, 57344, 8192) == DEC
     assert fq.auto_path(32, 57344, 8192) == DEC
+    assert fq.auto_path(48, 57344, 8192) == DEC
+    assert fq.auto_path(49, 57344, 8192) == PRE          # 448 column blocks
     assert fq.auto_path(33, 8192, 8192) == DEC           # 64 column blocks < 256 CUs
     assert fq.auto_path(64, 10240, 8192) == DEC          # 80 column blocks
     assert fq.auto_path(64, 57344, 8192) == PRE          # 448 column blocks

@@ -268,10 +268,12 @@ int device_cu_count() {
 }
 
 int auto_gemm_path(int64_t M, int64_t N) {
-  // Up to 32 tokens the weights are the whole cost: stream them.  From 33 to 64 the
-  // 128 x 128 prefill tile wins where it has a tile for every CU (wide layers); on
-  // narrow layers it would leave CUs idle and the streaming kernel is faster.
-  if (M <= 32) return 1;
+  // Up to 48 tokens (three 16-row blocks per pass) the streaming kernel is faster
+  // than any prefill tile on every LLaMA-2-70B layer (at M = 40: qkv 35 vs 39 us,
+  // o 24 vs 38, gate_up 110 vs 130, down 76 vs 126, weights cold).  From 49 to 64
+  // the prefill kernel wins where it has a 128 x 128 tile for every CU (wide
+  // layers); on narrow layers it would leave CUs idle and streaming is faster.
+  if (M <= 48) return 1;
   if (M <= kDecodeRowsPerPass && (N + 127) / 128 < device_cu_count()) return 1;
   return 2;
 }
