@@ -131,11 +131,10 @@ flexq_status flexq_gemm_w6ax(const int8_t* q_a, const float* s_a, const uint32_t
                              const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K,
                              int32_t group_size, int32_t abits, uint16_t* y_fp16, void* stream);
 
-/* The kernel FLEXQ_PATH_AUTO runs for an M x N x K product on the current device:
-   FLEXQ_PATH_DECODE (the weight-streaming kernel) for M <= 48, and for
-   M <= FLEXQ_DECODE_MAX_M when the prefill kernel's 128 x 128 tiles would number
-   fewer than the device's compute units; FLEXQ_PATH_PREFILL otherwise.  K does not
-   enter the choice.  Never fails (M <= 0 or N <= 0 report FLEXQ_PATH_DECODE). */
+/* The kernel FLEXQ_PATH_AUTO runs for an M x N x K product: FLEXQ_PATH_DECODE (the
+   weight-streaming kernel) for M <= FLEXQ_DECODE_MAX_M, FLEXQ_PATH_PREFILL above.
+   N and K do not enter the choice.  Never fails (M <= 0 or N <= 0 report
+   FLEXQ_PATH_DECODE). */
 int flexq_gemm_w6ax_auto_path(int64_t M, int64_t N, int64_t K);
 
 /* The tile FLEXQ_PATH_PREFILL uses for an M x N x K product on the current device

@@ -183,22 +183,18 @@ def test_binding_refuses_cpu_tensors():
 
 
 def test_auto_path_rule(flexq):
-    """The automatic kernel choice as flexq.h states it (with no GPU the CU count
-    falls back to MI355X's 256): decode up to 48 rows, decode up to 64 rows when the
-    128-wide prefill tiles would not cover the CUs, prefill otherwise."""
+    """The automatic kernel choice as flexq.h states it: the streaming kernel up to
+    one 64-row pass, the tiled kernel above, whatever the layer's width."""
     import w6a6_w6a8_integer_amd as fq
     DEC, PRE = fq.PATH_DECODE, fq.PATH_PREFILL
     assert fq.auto_path(1, 57344, 8192) == DEC
     assert fq.auto_path(32, 57344, 8192) == DEC
     assert fq.auto_path(48, 57344, 8192) == DEC
-    assert fq.auto_path(49, 57344, 8192) == PRE          # 448 column blocks
-    assert fq.auto_path(33, 8192, 8192) == DEC           # 64 column blocks < 256 CUs
-    assert fq.auto_path(64, 10240, 8192) == DEC          # 80 column blocks
-    assert fq.auto_path(64, 57344, 8192) == PRE          # 448 column blocks
-    assert fq.auto_path(64, 32768, 8192) == PRE          # exactly 256 column blocks
-    assert fq.auto_path(64, 32640, 8192) == DEC          # 255 column blocks
-    assert fq.auto_path(64, 32656, 8192) == PRE          # 256 (the last one partial)
+    assert fq.auto_path(64, 10240, 8192) == DEC
+    assert fq.auto_path(64, 57344, 8192) == DEC
+    assert fq.auto_path(64, 1 << 24, 128) == DEC
     assert fq.auto_path(65, 16, 128) == PRE
+    assert fq.auto_path(65, 57344, 8192) == PRE
     assert fq.auto_path(4096, 16, 128) == PRE
     assert fq.auto_path(0, 128, 128) == DEC
 

@@ -88,7 +88,15 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
   constexpr int COLS = T * 16;
   constexpr int OUTS = ROWS * COLS;
   constexpr int THREADS = 64 * S;
-  constexpr int OPT = (OUTS + THREADS - 1) / THREADS;
+  // Fold layout.  Up to 32 rows: dots parked row-major, one output per thread and
+  // round.  From 48 rows: parked column-major (padded pitch, conflict-free), each
+  // thread folding a 4-row segment of one column with 16-byte LDS reads: a quarter
+  // of the LDS instructions for the same register count.
+  constexpr bool QUAD = MT >= 3;
+  constexpr int PITCH = QUAD ? ROWS + 4 : COLS;  // int32s per parked column / row
+  constexpr int PARK = QUAD ? COLS * PITCH : OUTS;
+  constexpr int QUADS = (ROWS / 4) * COLS;
+  constexpr int OPT = QUAD ? 4 * ((QUADS + THREADS - 1) / THREADS) : (OUTS + THREADS - 1) / THREADS;
 
   const int G = K >> 7;
   const int lane = threadIdx.x & 63;
@@ -97,8 +105,8 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
   const int item_begin = blockIdx.x * per_wg;
   const int item_end = min(items, item_begin + per_wg);
 
-  __shared__ int32_t lds_d[2][S][OUTS];
-  __shared__ float lds_sa[2][S][ROWS];
+  __shared__ __attribute__((aligned(16))) int32_t lds_d[2][S][PARK];
+  __shared__ __attribute__((aligned(16))) float lds_sa[2][S][ROWS];
   __shared__ float lds_sw[2][S][COLS];
 
   const uint32_t a_lane_off = (uint32_t)(lane & 15) * (uint32_t)K + (uint32_t)(lane >> 4) * 16u;
@@ -194,11 +202,18 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int ms = 0; ms < MT; ++ms)
+        for (int ms = 0; ms < MT; ++ms) {
+          if constexpr (QUAD) {
+            *reinterpret_cast<i32x4*>(
+                &lds_d[slot][wave][(t * 16 + (lane & 15)) * PITCH + ms * 16 + 4 * (lane >> 4)]) =
+                d[t][ms];
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            lds_d[slot][wave][(ms * 16 + 4 * (lane >> 4) + i) * COLS + t * 16 + (lane & 15)] =
-                d[t][ms][i];
+            for (int i = 0; i < 4; ++i)
+              lds_d[slot][wave][(ms * 16 + 4 * (lane >> 4) + i) * COLS + t * 16 + (lane & 15)] =
+                  d[t][ms][i];
+          }
+        }
       if (lane < ROWS) lds_sa[slot][wave][lane] = b.sa;
       if (lane < COLS) lds_sw[slot][wave][lane] = 0.25f * half_bits_to_float((uint16_t)b.sw);
       // the step P ahead lands in this ring slot; it is the chunk's first item slot
@@ -211,6 +226,36 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
         const int row0 = cp.pass * 64;
         const int rows = min(ROWS, M - row0);
         const int ng = min(S, G - cp.r * S);
+        if constexpr (QUAD) {
+#pragma unroll
+          for (int j = 0; j < OPT / 4; ++j) {
+            const int q = threadIdx.x + j * THREADS;
+            const int col = q % COLS, r0 = 4 * (q / COLS);
+            if (q < QUADS && r0 < rows) {
+              i32x4 dv[S];
+              f32x4 sav[S];
+              float swv[S];
+#pragma unroll
+              for (int w = 0; w < S; ++w) {
+                dv[w] = *reinterpret_cast<const i32x4*>(&lds_d[slot][w][col * PITCH + r0]);
+                sav[w] = *reinterpret_cast<const f32x4*>(&lds_sa[slot][w][r0]);
+                swv[w] = lds_sw[slot][w][col];
+              }
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                float a = acc[ci][4 * j + r];
+#pragma unroll
+                for (int w = 0; w < S; ++w) {
+                  if (w < ng) {
+                    const float t = (float)dv[w][r] * swv[w];  // float(4d) is exact
+                    a = fmaf(t, sav[w][r], a);
+                  }
+                }
+                acc[ci][4 * j + r] = a;
+              }
+            }
+          }
+        } else {
 #pragma unroll
         for (int i = 0; i < OPT; ++i) {
           const int o = threadIdx.x + i * THREADS;
@@ -236,14 +281,28 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
             acc[ci][i] = a;
           }
         }
+        }
         if (cp.r == R - 1) {  // item complete: store and restart its accumulators
           const int tile = cp.tile0 + ci;
 #pragma unroll
           for (int i = 0; i < OPT; ++i) {
-            const int o = threadIdx.x + i * THREADS;
-            const int n = tile * COLS + o % COLS;
-            if (o < OUTS && o / COLS < rows && n < N)
-              y[(size_t)(row0 + o / COLS) * N + n] = float_to_half_bits(acc[ci][i]);
+            // output i of this thread: (row, col) in the item
+            int row, col;
+            bool in;
+            if constexpr (QUAD) {
+              const int q = threadIdx.x + (i / 4) * THREADS;
+              col = q % COLS;
+              row = 4 * (q / COLS) + i % 4;
+              in = q < QUADS;
+            } else {
+              const int o = threadIdx.x + i * THREADS;
+              col = o % COLS;
+              row = o / COLS;
+              in = o < OUTS;
+            }
+            const int n = tile * COLS + col;
+            if (in && row < rows && n < N)
+              y[(size_t)(row0 + row) * N + n] = float_to_half_bits(acc[ci][i]);
             acc[ci][i] = 0.0f;
           }
         }
@@ -268,14 +327,12 @@ int device_cu_count() {
 }
 
 int auto_gemm_path(int64_t M, int64_t N) {
-  // Up to 48 tokens (three 16-row blocks per pass) the streaming kernel is faster
-  // than any prefill tile on every LLaMA-2-70B layer (at M = 40: qkv 35 vs 39 us,
-  // o 24 vs 38, gate_up 110 vs 130, down 76 vs 126, weights cold).  From 49 to 64
-  // the prefill kernel wins where it has a 128 x 128 tile for every CU (wide
-  // layers); on narrow layers it would leave CUs idle and streaming is faster.
-  if (M <= 48) return 1;
-  if (M <= kDecodeRowsPerPass && (N + 127) / 128 < device_cu_count()) return 1;
-  return 2;
+  // Up to one 64-row pass the streaming kernel is faster than any prefill tile on
+  // every LLaMA-2-70B layer (M = 64, weights cold: qkv 37.5 vs 38.8 us, o 27 vs 37,
+  // gate_up 108 vs 121, down 87 vs 127); beyond it the weights would be streamed
+  // once per 64 rows and the tiled kernel wins.
+  (void)N;
+  return M <= kDecodeRowsPerPass ? 1 : 2;
 }
 
 template <int MT, int T, int S, int P, int C>
