@@ -88,11 +88,12 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
   constexpr int COLS = T * 16;
   constexpr int OUTS = ROWS * COLS;
   constexpr int THREADS = 64 * S;
-  // Fold layout.  Up to 32 rows: dots parked row-major, one output per thread and
-  // round.  From 48 rows: parked column-major (padded pitch, conflict-free), each
-  // thread folding a 4-row segment of one column with 16-byte LDS reads: a quarter
-  // of the LDS instructions for the same register count.
-  constexpr bool QUAD = MT >= 3;
+  // Fold layout.  With 16 waves (up to 32 rows): dots parked row-major, one output
+  // per thread and round.  With 8 waves or from 48 rows: parked column-major (padded
+  // pitch, conflict-free), each thread folding a 4-row segment of one column with
+  // 16-byte LDS reads: a quarter of the LDS instructions; the four accumulators per
+  // thread fit the 8-wave register budget.
+  constexpr bool QUAD = MT >= 3 || S <= 8;
   constexpr int PITCH = QUAD ? ROWS + 4 : COLS;  // int32s per parked column / row
   constexpr int PARK = QUAD ? COLS * PITCH : OUTS;
   constexpr int QUADS = (ROWS / 4) * COLS;
@@ -388,13 +389,20 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
     // fragment loads per weight byte and wins.
     if (N / 16 <= 3 * (int64_t)device_cu_count() && K <= 16384)
       return launch_decode_t<1, 1, 16, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
-    return launch_decode_t<1, 2, 16, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
+    // Paired tiles: 16 waves for up to 4 rows; from 5 rows 8 waves with the
+    // column-segment fold (70B down at M = 16: 39 -> 36 us; 16 waves stay faster
+    // at M = 1, where the fold is tiny and more waves keep more loads in flight).
+    if (rows <= 4) return launch_decode_t<1, 2, 16, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
+    return launch_decode_t<1, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
   }
   if (rows <= 32) {
-    // single tiles on narrow, short layers as above; then chunks of up to 4 items
+    // single tiles on narrow, short layers as above; then chunks of up to 4 items.
+    // Paired tiles take 8 waves: the register budget then allows chunks of 8 items
+    // (activation fragments shared 8 ways; 16 waves fit only 2) and the column-
+    // segment fold (70B gate_up at M = 24 / 32: 80 -> 67 / 90 -> 73 us).
     if (N / 16 <= 3 * (int64_t)device_cu_count() && K <= 16384)
       return launch_decode_t<2, 1, 16, 2, 4>(qa, sa, wp, sw, M, N, K, y, stream);
-    return launch_decode_t<2, 2, 16, 2, 2>(qa, sa, wp, sw, M, N, K, y, stream);
+    return launch_decode_t<2, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
   }
   if (rows <= 48) return launch_decode_t<3, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
   return launch_decode_t<4, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
