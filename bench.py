@@ -312,7 +312,10 @@ def main():
         # integer ops: the unit is TOP/s against the dense int8 MFMA peak
         roofline = {"kernel": "gemm_prefill_kernel", "bound": "mfma", "achieved": round(pre_tops, 1),
                     "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": round(pre_tops / INT8_PEAK_TOPS, 4),
-                    "traffic": recorded_traffic(), "launches_per_step": pre_launches,
+                    # counters were taken on the default workload's launches only
+                    "traffic": (recorded_traffic() if args.layers == "70b" and not args.m
+                                else None),
+                    "launches_per_step": pre_launches,
                     "ops_per_launch": round(pre_ops / len(step_ms) / max(pre_launches, 1))}
     else:
         roofline = {"kernel": "gemm_decode_kernel", "bound": "hbm", "achieved": round(dec_gbs, 1),
