@@ -52,7 +52,8 @@
  *
  * Preconditions: finite inputs; outputs must not overlap inputs; group_size == 128;
  * K a positive multiple of 128; N a multiple of 16; pointers aligned as stated.
- * The functions keep no mutable global state and may be called from any thread.
+ * The functions may be called from any thread.  Their only global state is a
+ * per-device cache of the compute-unit count, filled on first use (atomically).
  */
 #ifndef FLEXQ_H
 #define FLEXQ_H

@@ -3,7 +3,8 @@
 // Every entry point validates its arguments on the host before any HIP call and
 // returns an error without enqueuing anything; otherwise it enqueues the kernels on
 // the caller's stream and returns FLEXQ_SUCCESS (or FLEXQ_ERROR_LAUNCH if the runtime
-// rejected a launch).  No memory is allocated and no global state is kept.
+// rejected a launch).  No memory is allocated; the only global state is the
+// per-device compute-unit count that the launch geometry uses (gemm_decode.hip).
 #include "../../include/flexq.h"
 #include "kernels.h"
 

@@ -21,6 +21,8 @@
 // one barrier the block folds the S groups into the fp32 accumulators in
 // ascending group order, so the result equals the sequential definition bit for
 // bit.  The last round of an item stores its fp16 outputs.
+#include <atomic>
+
 #include "kernels.h"
 #include "w6_device.h"
 
@@ -314,17 +316,19 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
 }
 
 int device_cu_count() {
-  static int cached[64];  // per device; 0 = not yet queried
+  // per device, 0 = not yet queried; threads that race on the first query store the
+  // same value
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 int auto_gemm_path(int64_t M, int64_t N) {
