@@ -76,7 +76,8 @@ typedef enum {
   FLEXQ_PATH_AUTO = 0,    /* see flexq_gemm_w6ax_auto_path */
   FLEXQ_PATH_DECODE = 1,  /* HBM-streaming kernel for few tokens (any M is accepted) */
   FLEXQ_PATH_PREFILL = 2, /* MFMA-bound tiled kernel for many tokens (any M is accepted),
-                             tile chosen as flexq_gemm_w6ax_prefill_tile reports */
+                             tile chosen as flexq_gemm_w6ax_prefill_tile reports, with
+                             the tail split flexq_gemm_w6ax_prefill_main_cols reports */
   /* the prefill kernel with a fixed workgroup tile (rows x columns), for tests and
      tuning; every tile accepts every shape and gives the same bits */
   FLEXQ_PATH_PREFILL_256X128 = 3,
@@ -145,6 +146,15 @@ int flexq_gemm_w6ax_auto_path(int64_t M, int64_t N, int64_t K);
    no more than the compute units, else 128 x 128.  K does not enter the choice.
    Never fails. */
 int flexq_gemm_w6ax_prefill_tile(int64_t M, int64_t N, int64_t K);
+
+/* Tail split of FLEXQ_PATH_PREFILL.  When the 256 x 128 grid ends in a partly filled
+   round of one tile per compute unit, the 128-column blocks that fill whole rounds
+   run as one launch of that tile and the remaining columns as a second launch of
+   128 x 64 tiles on the same stream (at most two per compute unit), when the costs
+   measured for the tiles predict a saving of at least a twentieth.  Y is the same either way.  Returns how many
+   leading columns the first launch covers: N when there is no split, 0 for
+   N <= 0.  K does not enter the choice.  Never fails. */
+int64_t flexq_gemm_w6ax_prefill_main_cols(int64_t M, int64_t N, int64_t K);
 
 /* flexq_gemm_w6ax with an explicit kernel choice (flexq_path); every kernel and
    tile accepts every M and gives identical results. */

@@ -219,6 +219,33 @@ def test_prefill_tile_rule(flexq):
     assert fq.prefill_tile(0, 16, 128) == T64
 
 
+def test_prefill_tail_split_rule(flexq):
+    """The tail split as flexq.h states it (256 CUs without a GPU): whole rounds of
+    256 x 128 tiles over the leading columns, 128 x 64 tiles for the rest, when the
+    stated costs (a round 1.0; 128 x 64 tiles 0.48 up to one per CU, plus 0.6 per
+    further CU's worth, at most two per CU) save 5 %."""
+    import w6a6_w6a8_integer_amd as fq
+    mc = fq.prefill_main_cols
+    # 4 x 80 = 320 tiles: 256 in one round (64 column blocks), 2048 columns of
+    # 128 x 64 tiles (8 x 32 = 256, one per CU): 1.48 rounds instead of 2
+    assert mc(1024, 10240, 8192) == 8192
+    assert mc(1024, 27648, 5120) == 24576                # 3 + 0.78 (1.5 per CU) vs 4
+    assert mc(1000, 10192, 128) == 8192                  # ragged M and N
+    assert mc(520, 33280, 128) == 32768                  # 3 row blocks: 85 column blocks
+    assert mc(8192, 1280, 8192) == 1024                  # 64 x 10 tiles: 1 + 0.48 vs 3
+    # whole rounds already, or a tail that costs more than it saves
+    assert mc(4096, 57344, 8192) == 57344                # 7168 tiles = 28 rounds
+    assert mc(1024, 8192, 8192) == 8192                  # 256 tiles, one round
+    assert mc(256, 57344, 8192) == 57344                 # 1 + 2 x 0.685 > 2
+    assert mc(512, 57344, 8192) == 57344                 # 3 + 1.08 (2 per CU) vs 4
+    assert mc(4096, 7168, 8192) == 7168                  # 3 + 1.08 vs 4
+    assert mc(2048, 10240, 8192) == 10240                # 2 + 1.08 vs 3
+    # other tiles, empty shapes
+    assert mc(256, 8192, 28672) == 8192                  # 128 x 64 grid
+    assert mc(64, 57344, 8192) == 57344                  # 128 x 128 grid
+    assert mc(0, 16, 128) == 16 and mc(16, 0, 128) == 0
+
+
 def test_gemm_path_values(flexq):
     f = flexq.flexq_gemm_w6ax_path
     for bad in (-1, 6, 7):

@@ -48,6 +48,7 @@ SIGNATURES = {
     "flexq_gemm_w6ax_group_dots": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _P, _P]),
     "flexq_gemm_w6ax_auto_path": (ctypes.c_int, [_I64, _I64, _I64]),
     "flexq_gemm_w6ax_prefill_tile": (ctypes.c_int, [_I64, _I64, _I64]),
+    "flexq_gemm_w6ax_prefill_main_cols": (ctypes.c_int64, [_I64, _I64, _I64]),
     "flexq_linear_w6ax_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "flexq_linear_w6ax": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P,
                                          ctypes.c_size_t, _P, _P]),
@@ -190,6 +191,12 @@ def prefill_tile(M: int, N: int, K: int) -> int:
     """PATH_PREFILL_256X128 / _128X128 / _128X64: the tile PATH_PREFILL uses for this
     shape on the current device (flexq_gemm_w6ax_prefill_tile)."""
     return int(lib().flexq_gemm_w6ax_prefill_tile(M, N, K))
+
+
+def prefill_main_cols(M: int, N: int, K: int) -> int:
+    """Columns the first PATH_PREFILL launch covers on the current device; N unless
+    a second launch of 128 x 64 tiles takes the rest (flexq_gemm_w6ax_prefill_main_cols)."""
+    return int(lib().flexq_gemm_w6ax_prefill_main_cols(M, N, K))
 
 
 def auto_path(M: int, N: int, K: int) -> int:

@@ -174,6 +174,12 @@ int flexq_gemm_w6ax_prefill_tile(int64_t M, int64_t N, int64_t K) {
                                     : FLEXQ_PATH_PREFILL_128X64;
 }
 
+int64_t flexq_gemm_w6ax_prefill_main_cols(int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  if (M <= 0 || N <= 0) return N > 0 ? N : 0;
+  return flexq::prefill_main_cols(M, N);
+}
+
 int flexq_gemm_w6ax_auto_path(int64_t M, int64_t N, int64_t K) {
   (void)K;  // the choice depends on the token count and the layer width only
   if (M <= 0 || N <= 0) return FLEXQ_PATH_DECODE;

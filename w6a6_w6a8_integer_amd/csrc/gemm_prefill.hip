@@ -41,6 +41,7 @@
 // Workgroups are numbered so that the 8 XCDs each take a contiguous run of
 // logical tiles (hardware hands workgroup i to XCD i % 8), and logical tiles run
 // over a band of GM row blocks before moving to the next column block.
+#include <algorithm>
 #include <utility>
 
 #include "kernels.h"
@@ -124,7 +125,8 @@ struct PrefillCfg {
 template <int BM, int BN>
 __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint32_t* __restrict__ wp,
-    const uint16_t* __restrict__ sw, int M, int N, int K, int GM, uint16_t* __restrict__ y) {
+    const uint16_t* __restrict__ sw, int M, int N, int K, int ldn, int GM,
+    uint16_t* __restrict__ y) {
   using C = PrefillCfg<BM, BN>;
   constexpr int TN = C::TN;
   static_assert(TN == 1 || TN == 2, "one or two 32-column tiles per wave");
@@ -160,9 +162,10 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // Out-of-range loads return zero: rows >= M and columns >= N vanish.
   const auto ra = make_rsrc(qa + (size_t)m0 * K, (uint32_t)mrows * (uint32_t)K);
   const auto rw = make_rsrc(wp + (size_t)(n0 / 16) * 3 * K, (uint32_t)(ncols / 16) * 12u * K);
-  // scales are group-major: s_a[g][m] at g*M + m, s_w[g][n] at g*N + n
+  // scales are group-major: s_a[g][m] at g*M + m, s_w[g][n] at g*ldn + n (the launch
+  // covers columns 0 .. N-1 of a matrix whose Y rows and s_w rows are ldn apart)
   const auto rsa = make_rsrc(sa + m0, (uint32_t)((size_t)G * M - m0) * 4u);
-  const auto rsw = make_rsrc(sw + n0, (uint32_t)((size_t)G * N - n0) * 2u);
+  const auto rsw = make_rsrc(sw + n0, (uint32_t)((size_t)(G - 1) * ldn + N - n0) * 2u);
 
   // A stage: row-major, 128 bytes per row, the 16-byte chunk j of row r stored at
   // chunk j ^ ((r >> 1) & 7) (so the 32x32 fragment reads below touch every bank
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
 #pragma unroll
     for (int i = 0; i < C::B_UNITS; ++i)
       r.u[i] = __builtin_amdgcn_raw_buffer_load_b96(rw, b_voff_u[i], (uint32_t)g * 1536u, 0);
-    r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u, 0, 0);
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)ldn * 2u, 0, 0);
   };
   auto issue_dma = [&](int g, int so) {
     int8_t* la = lds + so;
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
                                                         0);
     } else {
       if constexpr (kRole == kRoleSw)
-        r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)N * 2u,
+        r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)ldn * 2u,
                                                    0, 0);
     }
   };
@@ -522,8 +525,8 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // in LDS (its own region, row pitch kOutPitch) and stores every row as 16-byte
   // chunks: 4TN store instructions per lane instead of 32TN two-byte ones.  The barrier
   // lets no wave overwrite a stage while another wave's copies into it may still
-  // land.  (N is a multiple of 16, so an 8-column chunk is wholly inside or outside
-  // the matrix and every row starts 16-byte aligned.)
+  // land.  (N and ldn are multiples of 16, so an 8-column chunk is wholly inside or
+  // outside the matrix and every row starts 16-byte aligned.)
   if ((reinterpret_cast<uintptr_t>(y) & 15u) == 0) {
     barrier();
     uint8_t* tw = reinterpret_cast<uint8_t*>(lds) + wave * 64 * kOutPitch;
@@ -546,7 +549,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
       const i32x4 v = *reinterpret_cast<const i32x4*>(tw + lr * kOutPitch + (lane % CH) * 16);
       const int row = wm * 64 + lr;
       if (row < mrows && col < ncols)
-        *reinterpret_cast<i32x4*>(y + (size_t)(m0 + row) * N + n0 + col) = v;
+        *reinterpret_cast<i32x4*>(y + (size_t)(m0 + row) * ldn + n0 + col) = v;
     }
     return;
   }
@@ -561,20 +564,33 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
         for (int r = 0; r < 16; ++r) {
           const int row = wm * 64 + tm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (row < mrows)
-            y[(size_t)(m0 + row) * N + n0 + col] = float_to_half_bits(acc[tm][tn][r]);
+            y[(size_t)(m0 + row) * ldn + n0 + col] = float_to_half_bits(acc[tm][tn][r]);
         }
       }
     }
 }
 
+// Columns n0 .. n0 + N - 1 of a product whose Y and s_w rows are ldn columns apart.
 template <int BM, int BN>
 static void launch_prefill_t(const int8_t* qa, const float* sa, const uint32_t* wp,
-                             const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
-                             hipStream_t stream) {
+                             const uint16_t* sw, int64_t M, int64_t n0, int64_t N, int64_t K,
+                             int64_t ldn, uint16_t* y, hipStream_t stream) {
   const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   const int GM = 4;
   hipLaunchKernelGGL((gemm_prefill_kernel<BM, BN>), dim3((unsigned)(nbm * nbn)), dim3(BM * 2), 0,
-                     stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, GM, y);
+                     stream, qa, sa, wp + (n0 / 16) * 3 * K, sw + n0, (int)M, (int)N, (int)K,
+                     (int)ldn, GM, y + n0);
+}
+
+static void launch_tile(int tile, const int8_t* qa, const float* sa, const uint32_t* wp,
+                        const uint16_t* sw, int64_t M, int64_t n0, int64_t N, int64_t K,
+                        int64_t ldn, uint16_t* y, hipStream_t stream) {
+  if (tile == kTile256x128)
+    launch_prefill_t<256, 128>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
+  else if (tile == kTile128x128)
+    launch_prefill_t<128, 128>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
+  else
+    launch_prefill_t<128, 64>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
 }
 
 int prefill_tile(int64_t M, int64_t N) {
@@ -595,23 +611,46 @@ int prefill_tile(int64_t M, int64_t N) {
   return tiles128 <= cu ? kTile128x64 : kTile128x128;
 }
 
+int64_t prefill_main_cols(int64_t M, int64_t N) {
+  // When the 256 x 128 grid ends in a partly filled round, the 128-column blocks that
+  // fill whole rounds run as 256 x 128 tiles and the remaining columns as a second
+  // launch of 128 x 64 tiles, if that is expected to save a twentieth.  Costs in
+  // rounds of 256 x 128 tiles, measured on 70B-sized layers (K = 4096 to 8192): up to
+  // one 128 x 64 tile per CU 0.48, and 0.6 more per further CU's worth of them (0.74
+  // for 1.5 per CU, 1.1 to 1.5 for 2 per CU); tails of more than 2 per CU are not
+  // split off.  (A round of 128 x 128 tiles costs about 0.685 for half the columns of
+  // a round of 128 x 64 tiles, so it is never the better tail.)
+  if (prefill_tile(M, N) != kTile256x128) return N;
+  const int64_t cu = device_cu_count();
+  const int64_t nbm = (M + 255) / 256, nbn = (N + 127) / 128, tiles = nbm * nbn;
+  const int64_t full = tiles / cu;  // whole rounds
+  if (full == 0 || tiles % cu == 0) return N;
+  const int64_t c = full * cu / nbm;  // column blocks that fit in whole rounds
+  if (c == 0 || c >= nbn) return N;
+  const int64_t main_rounds = (nbm * c + cu - 1) / cu;
+  const int64_t n64 = (M + 127) / 128 * ((N - 128 * c + 63) / 64);  // tail tiles
+  if (n64 > 2 * cu) return N;
+  const int64_t tail = n64 <= cu ? 480 : 480 + (n64 - cu) * 600 / cu;
+  const int64_t split = main_rounds * 1000 + tail;
+  return split * 20 <= (full + 1) * 1000 * 19 ? 128 * c : N;
+}
+
 hipError_t launch_gemm_prefill(const int8_t* qa, const float* sa, const uint32_t* wp,
                                const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                                hipStream_t stream, int tile) {
-  if (tile == kTileAuto) tile = prefill_tile(M, N);
-  switch (tile) {
-    case kTile256x128:
-      launch_prefill_t<256, 128>(qa, sa, wp, sw, M, N, K, y, stream);
-      break;
-    case kTile128x128:
-      launch_prefill_t<128, 128>(qa, sa, wp, sw, M, N, K, y, stream);
-      break;
-    case kTile128x64:
-      launch_prefill_t<128, 64>(qa, sa, wp, sw, M, N, K, y, stream);
-      break;
-    default:
-      return hipErrorInvalidValue;
+  if (tile == kTileAuto) {
+    const int64_t n_main = prefill_main_cols(M, N);
+    launch_tile(prefill_tile(M, N), qa, sa, wp, sw, M, 0, n_main, K, N, y, stream);
+    if (n_main < N) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      launch_tile(kTile128x64, qa, sa, wp, sw, M, n_main, N - n_main, K, N, y, stream);
+    }
+    return hipGetLastError();
   }
+  if (tile != kTile256x128 && tile != kTile128x128 && tile != kTile128x64)
+    return hipErrorInvalidValue;
+  launch_tile(tile, qa, sa, wp, sw, M, 0, N, K, N, y, stream);
   return hipGetLastError();
 }
 

@@ -21,6 +21,9 @@ constexpr int kTileAuto = 0, kTile256x128 = 1, kTile128x128 = 2, kTile128x64 = 3
 
 // The tile the prefill kernel uses for an M x N product on the current device.
 int prefill_tile(int64_t M, int64_t N);
+// columns the main prefill launch covers (N unless a launch of 128 x 64 tiles takes
+// the rest)
+int64_t prefill_main_cols(int64_t M, int64_t N);
 
 hipError_t launch_gemm_prefill(const int8_t* qa, const float* sa, const uint32_t* wp,
                                const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
