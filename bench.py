@@ -292,6 +292,9 @@ def main():
             "kernel": "decode" if fq.auto_path(M, N, K) == fq.PATH_DECODE else "prefill",
             "tile": (None if fq.auto_path(M, N, K) == fq.PATH_DECODE else
                      TILE_NAMES[fq.prefill_tile(M, N, K)]),
+            # columns a second prefill launch of 128 x 64 tiles covers (tail split)
+            "tail_cols": (N - fq.prefill_main_cols(M, N, K)
+                          if fq.auto_path(M, N, K) == fq.PATH_PREFILL else 0),
             "gemm_us": round(g * 1e3, 2), "quant_us": round(q * 1e3, 2),
             "tops": round(ops / (g * 1e-3) / 1e12, 2),
             "gbs": round(by / (g * 1e-3) / 1e9, 1),
@@ -305,8 +308,12 @@ def main():
     value = tot_ops / (ms_per_step * 1e-3) / 1e12
 
     pre_tops = pre_ops / (pre_ms * 1e-3) / 1e12 if pre_ms else 0.0
+    # a prefill GEMM call is one kernel launch, two when the tail split applies
     pre_launches = sum(1 for (M, _, name, _) in plan
                        if fq.auto_path(M, *LAYERS[name]) == fq.PATH_PREFILL)
+    pre_kernels = sum(1 + (fq.prefill_main_cols(M, *LAYERS[name]) < LAYERS[name][0])
+                      for (M, _, name, _) in plan
+                      if fq.auto_path(M, *LAYERS[name]) == fq.PATH_PREFILL)
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9 if dec_ms else 0.0
     if pre_ms >= dec_ms:
         # integer ops: the unit is TOP/s against the dense int8 MFMA peak
@@ -316,6 +323,7 @@ def main():
                     "traffic": (recorded_traffic() if args.layers == "70b" and not args.m
                                 else None),
                     "launches_per_step": pre_launches,
+                    "kernel_launches_per_step": pre_kernels,
                     "ops_per_launch": round(pre_ops / len(step_ms) / max(pre_launches, 1))}
     else:
         roofline = {"kernel": "gemm_decode_kernel", "bound": "hbm", "achieved": round(dec_gbs, 1),
