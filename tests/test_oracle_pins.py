@@ -445,3 +445,101 @@ def test_quantized_layer_tracks_fp64_reference():
         y = oracle.gemm(qa, sa, qw, sw).astype(np.float64)
         nmse = np.sum((y - ref) ** 2) / np.sum(ref ** 2)
         assert nmse < limit, (abits, nmse)
+
+
+# ---------------------------------------------------------------------------
+# worked vectors (tests/golden/worked_vectors.txt), re-derived here in exact
+# rational arithmetic before the oracle is compared with them
+# ---------------------------------------------------------------------------
+
+def _golden_vectors():
+    ramp, e2e = None, {}
+    with open(os.path.join(GOLDEN, "worked_vectors.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = [p.strip() for p in line.split(";")]
+            if parts[0] == "w6_ramp":
+                ramp = (int(parts[1].split()[1], 16), [int(v) for v in parts[2].split()[1:]],
+                        [int(v) for v in parts[3].split()[1:]])
+            elif parts[0] == "e2e":
+                e2e[int(parts[1])] = dict(
+                    d=[int(v) for v in parts[2].split()],
+                    sa=[int(v, 16) for v in parts[3].split()],
+                    sw=[int(v, 16) for v in parts[4].split()],
+                    acc=int(parts[5], 16), y=int(parts[6], 16))
+    return ramp, e2e
+
+
+def _exact_codes(vals, scale, qmax):
+    """round_half_even(v / scale) in exact rationals, clamped; a quotient within
+    2^-18 of a rounding boundary is left to the IEEE binary32 quotient (numpy)."""
+    out = []
+    for v in vals:
+        quo = Fraction(float(v)) / Fraction(float(scale))
+        q = int(np.rint(np.float32(v) / np.float32(scale))) if _near_tie(quo) else round(quo)
+        out.append(max(-qmax, min(qmax, q)))
+    return out
+
+
+def _worked_inputs():
+    k = np.arange(G)
+    x = np.zeros((1, 2 * G), np.float16)
+    w = np.zeros((16, 2 * G), np.float16)
+    x[0, :G] = (k - 64) / 64.0
+    w[0, :G] = 0.05 * (k - 64) / 64.0
+    x[0, G:] = -3.0 * (63 - k) / 64.0
+    w[0, G:] = 0.02 * np.sin(k.astype(np.float64))
+    return x, w
+
+
+def test_w6_ramp_worked_vector():
+    s16_bits, head, tail = _golden_vectors()[0]
+    k = np.arange(G)
+    w = np.zeros((16, G), np.float16)
+    w[0] = 0.05 * (k - 64) / 64.0
+    # independent derivation: IEEE division (numpy), fp16 rounding, exact rational codes
+    amax = np.max(np.abs(w[0].astype(np.float32)))
+    s16 = (np.float32(amax) / np.float32(31)).astype(np.float16)
+    assert int(s16.view(np.uint16)) == s16_bits
+    codes = _exact_codes(w[0], s16, 31)
+    assert codes[:4] == head and codes[124:] == tail
+    qw, sw = oracle.quant_w6(w)
+    assert int(sw[0, 0].view(np.uint16)) == s16_bits
+    assert list(qw[0]) == codes
+
+
+@pytest.mark.parametrize("abits", [6, 8])
+def test_end_to_end_worked_vector(abits):
+    ref = _golden_vectors()[1][abits]
+    qmax = 31 if abits == 6 else 127
+    x, w = _worked_inputs()
+    # independent derivation of every intermediate
+    acc = np.float32(0.0)
+    for g in range(2):
+        xs, ws = x[0, g * G:(g + 1) * G], w[0, g * G:(g + 1) * G]
+        s_a = np.float32(np.max(np.abs(xs.astype(np.float32)))) / np.float32(qmax)
+        s16 = (np.float32(np.max(np.abs(ws.astype(np.float32)))) / np.float32(31)).astype(np.float16)
+        qa = _exact_codes(xs, s_a, qmax)
+        qw = _exact_codes(ws, s16, 31)
+        d = sum(a * b for a, b in zip(qa, qw))
+        assert d == ref["d"][g]
+        assert int(s_a.view(np.uint32)) == ref["sa"][g]
+        assert int(s16.view(np.uint16)) == ref["sw"][g]
+        t = _fp32_round(Fraction(d) * Fraction(float(s16)))
+        acc = _fp32_round(Fraction(float(t)) * Fraction(float(s_a)) + Fraction(float(acc)))
+    assert int(acc.view(np.uint32)) == ref["acc"]
+    assert int(np.float32(acc).astype(np.float16).view(np.uint16)) == ref["y"]
+    # the oracle, step by step
+    qa, sa = oracle.quant_act(x, abits)
+    qw, sw = oracle.quant_w6(w)
+    assert [int(v) for v in sa[0].view(np.uint32)] == ref["sa"]
+    assert [int(v) for v in sw[0].view(np.uint16)] == ref["sw"]
+    assert list(oracle.group_dots(qa, qw[:1])[0, 0]) == ref["d"]
+    y, acc_o, _ = oracle.gemm(qa, sa, qw[:1], sw[:1], want_acc=True)
+    assert int(acc_o[0, 0].view(np.uint32)) == ref["acc"]
+    assert int(y[0, 0].view(np.uint16)) == ref["y"]
+    # the same through the packed weights
+    wp, sw2 = oracle.pack_w6(w)
+    assert int(oracle.gemm_packed(qa, sa, wp, sw2, 16)[0, 0].view(np.uint16)) == ref["y"]
