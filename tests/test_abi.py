@@ -182,6 +182,86 @@ def test_binding_refuses_cpu_tensors():
         fq.quant_act(torch.zeros(2, 128, dtype=torch.float16), 6)
 
 
+def _good_gemm_args(M=3, N=32, K=256):
+    import torch
+    G = K // 128
+    return dict(q_a=torch.zeros(M, K, dtype=torch.int8),
+                s_a=torch.zeros(G, M, dtype=torch.float32),
+                w_packed=torch.zeros(3 * N * K // 16, dtype=torch.int32),
+                s_w=torch.zeros(G, N, dtype=torch.float16), N=N, abits=6,
+                y=torch.zeros(M, N, dtype=torch.float16))
+
+
+@pytest.mark.parametrize("field,bad,err,match", [
+    ("s_a", ("zeros", (3, 2), "float32"), ValueError, "s_a must have shape"),   # [M][G]
+    ("s_a", ("zeros", (2, 3), "float16"), TypeError, "s_a must be"),
+    ("s_w", ("zeros", (32, 2), "float16"), ValueError, "s_w must have shape"),  # [N][G]
+    ("s_w", ("zeros", (2, 32), "float32"), TypeError, "s_w must be"),
+    ("w_packed", ("zeros", (3 * 32 * 256 // 16 - 1,), "int32"), ValueError, "w_packed holds"),
+    ("w_packed", ("zeros", (3 * 32 * 256 // 16,), "uint8"), TypeError, "w_packed must be"),
+    ("w_packed", ("zeros", (48, 32), "int32"), ValueError, "w_packed must be 1-D"),
+    ("y", ("zeros", (3, 16), "float16"), ValueError, "y must have shape"),
+    ("y", ("zeros", (3, 32), "float32"), TypeError, "y must be"),
+    ("q_a", ("zeros", (3, 200), "int8"), ValueError, "multiple of 128"),
+    ("q_a", ("zeros", (768,), "int8"), ValueError, "2-D"),
+    ("N", 40, ValueError, "multiple of 16"),
+])
+def test_binding_checks_every_gemm_argument_before_any_call(field, bad, err, match):
+    """Every tensor argument is checked (dtype, exact shape or size, contiguity,
+    device) in Python before the C ABI sees a pointer: a wrong buffer raises instead
+    of reading or writing out of bounds on the GPU."""
+    import torch
+    import w6a6_w6a8_integer_amd as fq
+    args = _good_gemm_args()
+    if isinstance(bad, tuple):
+        _, shape, dt = bad
+        args[field] = torch.zeros(shape, dtype=getattr(torch, dt))
+    else:
+        args[field] = bad
+    with pytest.raises(err, match=match):
+        fq.gemm_w6ax(**args)
+
+
+def test_binding_checks_shapes_then_device():
+    """With every shape right, the remaining objection to host tensors is the device."""
+    import torch
+    import w6a6_w6a8_integer_amd as fq
+    with pytest.raises(TypeError, match="CUDA"):
+        fq.gemm_w6ax(**_good_gemm_args())
+    a = _good_gemm_args()
+    nc = torch.zeros(a["N"], a["q_a"].shape[0], dtype=torch.float16).t()   # non-contiguous
+    with pytest.raises(ValueError, match="contiguous"):
+        fq.gemm_w6ax(**{**a, "y": nc})
+
+
+def test_binding_checks_the_other_entry_points():
+    import torch
+    import w6a6_w6a8_integer_amd as fq
+    f16, i8, i32, u8, f32 = torch.float16, torch.int8, torch.int32, torch.uint8, torch.float32
+    x = torch.zeros(2, 256, dtype=f16)
+    with pytest.raises(ValueError, match="q_a must have shape"):
+        fq.quant_act(x, 6, q_a=torch.zeros(2, 128, dtype=i8))
+    with pytest.raises(ValueError, match="s_a must have shape"):
+        fq.quant_act(x, 6, q_a=torch.zeros(2, 256, dtype=i8), s_a=torch.zeros(2, 2, dtype=f32)[:1])
+    with pytest.raises(ValueError, match="s_w must have shape"):
+        fq.pack_w6(torch.zeros(32, 256, dtype=f16), s_w=torch.zeros(32, 2, dtype=f16))
+    with pytest.raises(ValueError, match="w_packed holds"):
+        fq.pack_w6(torch.zeros(32, 256, dtype=f16), w_packed=torch.zeros(10, dtype=i32))
+    with pytest.raises(ValueError, match="multiple of 16"):
+        fq.pack_w6(torch.zeros(24, 256, dtype=f16))
+    wp = torch.zeros(3 * 32 * 256 // 16, dtype=i32)
+    sw = torch.zeros(2, 32, dtype=f16)
+    with pytest.raises(ValueError, match="workspace holds"):
+        fq.linear_w6ax(x, wp, sw, 32, 6, workspace=torch.zeros(16, dtype=u8))
+    with pytest.raises(ValueError, match="y must have shape"):
+        fq.linear_w6ax(x, wp, sw, 32, 6, y=torch.zeros(32, 2, dtype=f16))
+    with pytest.raises(ValueError, match="dots must have shape"):
+        fq.gemm_w6ax_group_dots(torch.zeros(2, 256, dtype=i8), wp, 32,
+                                dots=torch.zeros(2, 32, 1, dtype=i32))
+    with pytest.raises(TypeError, match="CUDA"):
+        fq.gemm_w6ax_group_dots(torch.zeros(2, 256, dtype=i8), wp, 32)
+
+
 def test_auto_path_rule(flexq):
     """The automatic kernel choice as flexq.h states it: the streaming kernel up to
     one 64-row pass, the tiled kernel above, whatever the layer's width."""

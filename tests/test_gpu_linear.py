@@ -149,7 +149,9 @@ def test_linear_rejects_bad_arguments_before_launch(fq):
     w = synth.weights(synth.derive_seed(35, "w"), N, K)
     wp, sw = fq.pack_w6(to_dev(w))
     x = to_dev(synth.activations(synth.derive_seed(35, "x"), 8, K))
-    with pytest.raises(fq.FlexqError, match="INVALID"):
+    # a workspace that is too small is refused by the binding (the C ABI refuses it
+    # too: the ctypes tests of the ABI call it directly)
+    with pytest.raises(ValueError, match="workspace"):
         fq.linear_w6ax(x, wp, sw, N, 8,
                        workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     xu = torch.empty(2 * K + 4, dtype=torch.float16, device=DEV)[4:].view(2, K)  # 8 B past

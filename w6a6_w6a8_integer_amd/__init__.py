@@ -90,14 +90,63 @@ def _stream(t: torch.Tensor | None = None) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-def _cuda(t: torch.Tensor, dtype, name: str):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+def _tensor(t, dtype, name: str, shape=None, min_bytes=None):
+    """Check one tensor argument before anything reaches the C ABI, which sees only
+    pointers and cannot tell a wrong buffer from a right one: type, dtype, exact
+    shape (or a minimum size for flat buffers) and contiguity.  Where the tensors
+    live is checked once for all of them (_on_gpu), after every shape."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes; "
+                         f"at least {min_bytes} are needed")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _on_gpu(**tensors):
+    """Every argument is a CUDA (HIP) tensor, all on one device; returns it."""
+    dev = None
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
+    return dev
+
+
+def _matrix(t, dtype, name: str):
+    """A 2-D tensor argument whose shape defines the problem size."""
+    if isinstance(t, torch.Tensor) and t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return _tensor(t, dtype, name)
+
+
+def _groups(K: int, name: str) -> int:
+    if K <= 0 or K % GROUP:
+        raise ValueError(f"{name}: K = {K} must be a positive multiple of {GROUP}")
+    return K // GROUP
+
+
+def _cols(N: int) -> int:
+    N = int(N)
+    if N < 0 or N % 16:
+        raise ValueError(f"N = {N} must be a non-negative multiple of 16")
+    return N
+
+
+def _packed(w_packed, N: int, K: int):
+    """Packed weights: a flat int32 buffer of at least 0.75 * N * K bytes."""
+    if isinstance(w_packed, torch.Tensor) and w_packed.dim() != 1:
+        raise ValueError(f"w_packed must be 1-D, got shape {tuple(w_packed.shape)}")
+    return _tensor(w_packed, torch.int32, "w_packed", min_bytes=3 * N * K // 4)
 
 
 def packed_w6_bytes(N: int, K: int) -> int:
@@ -112,12 +161,17 @@ def pack_w6(w: torch.Tensor, w_packed: torch.Tensor | None = None,
             s_w: torch.Tensor | None = None):
     """fp16 W[N][K] -> (w_packed int32[3*N*K/16] holding the packed dwords,
     s_w fp16[K/128][N], group-major)."""
-    _cuda(w, torch.float16, "w")
+    _matrix(w, torch.float16, "w")
     N, K = w.shape
+    G = _groups(K, "pack_w6")
+    _cols(N)
     if w_packed is None:
-        w_packed = torch.empty(max(1, packed_w6_words(N, K)), dtype=torch.int32, device=w.device)
+        w_packed = torch.empty(max(1, 3 * N * K // 16), dtype=torch.int32, device=w.device)
     if s_w is None:
-        s_w = torch.empty((K // GROUP, N), dtype=torch.float16, device=w.device)
+        s_w = torch.empty((G, N), dtype=torch.float16, device=w.device)
+    _packed(w_packed, N, K)
+    _tensor(s_w, torch.float16, "s_w", shape=(G, N))
+    _on_gpu(w=w, w_packed=w_packed, s_w=s_w)
     _check(lib().flexq_pack_w6(w.data_ptr(), N, K, GROUP, w_packed.data_ptr(), s_w.data_ptr(),
                                _stream(w)), "flexq_pack_w6")
     return w_packed, s_w
@@ -126,12 +180,16 @@ def pack_w6(w: torch.Tensor, w_packed: torch.Tensor | None = None,
 def quant_act(x: torch.Tensor, abits: int, q_a: torch.Tensor | None = None,
               s_a: torch.Tensor | None = None):
     """fp16 X[M][K] -> (q_a int8[M][K], s_a fp32[K/128][M], group-major); abits 6 or 8."""
-    _cuda(x, torch.float16, "x")
+    _matrix(x, torch.float16, "x")
     M, K = x.shape
+    G = _groups(K, "quant_act")
     if q_a is None:
         q_a = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if s_a is None:
-        s_a = torch.empty((K // GROUP, M), dtype=torch.float32, device=x.device)
+        s_a = torch.empty((G, M), dtype=torch.float32, device=x.device)
+    _tensor(q_a, torch.int8, "q_a", shape=(M, K))
+    _tensor(s_a, torch.float32, "s_a", shape=(G, M))
+    _on_gpu(x=x, q_a=q_a, s_a=s_a)
     _check(lib().flexq_quant_act(x.data_ptr(), M, K, GROUP, abits, q_a.data_ptr(),
                                  s_a.data_ptr(), _stream(x)), "flexq_quant_act")
     return q_a, s_a
@@ -139,11 +197,20 @@ def quant_act(x: torch.Tensor, abits: int, q_a: torch.Tensor | None = None,
 
 def gemm_w6ax(q_a: torch.Tensor, s_a: torch.Tensor, w_packed: torch.Tensor, s_w: torch.Tensor,
               N: int, abits: int, y: torch.Tensor | None = None, path: int = PATH_AUTO):
-    """Y fp16[M][N] from quantized activations and packed weights."""
-    _cuda(q_a, torch.int8, "q_a")
+    """Y fp16[M][N] from quantized activations (q_a int8[M][K], s_a fp32[K/128][M])
+    and packed weights (w_packed, s_w fp16[K/128][N])."""
+    _matrix(q_a, torch.int8, "q_a")
     M, K = q_a.shape
+    G = _groups(K, "gemm_w6ax")
+    N = _cols(N)
+    dev = q_a.device
+    _tensor(s_a, torch.float32, "s_a", shape=(G, M))
+    _packed(w_packed, N, K)
+    _tensor(s_w, torch.float16, "s_w", shape=(G, N))
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=q_a.device)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    _tensor(y, torch.float16, "y", shape=(M, N))
+    _on_gpu(q_a=q_a, s_a=s_a, w_packed=w_packed, s_w=s_w, y=y)
     _check(lib().flexq_gemm_w6ax_path(q_a.data_ptr(), s_a.data_ptr(), w_packed.data_ptr(),
                                       s_w.data_ptr(), M, N, K, GROUP, abits, path, y.data_ptr(),
                                       _stream(q_a)), "flexq_gemm_w6ax")
@@ -159,28 +226,42 @@ def linear_w6ax(x: torch.Tensor, w_packed: torch.Tensor, s_w: torch.Tensor, N: i
     """Y fp16[M][N] from fp16 X[M][K] and packed weights (flexq_linear_w6ax); the
     workspace (uint8, at least linear_w6ax_workspace_bytes(M, K)) is allocated here
     when the caller does not pass one."""
-    _cuda(x, torch.float16, "x")
+    _matrix(x, torch.float16, "x")
     M, K = x.shape
+    G = _groups(K, "linear_w6ax")
+    N = _cols(N)
+    dev = x.device
+    _packed(w_packed, N, K)
+    _tensor(s_w, torch.float16, "s_w", shape=(G, N))
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    _tensor(y, torch.float16, "y", shape=(M, N))
+    need = linear_w6ax_workspace_bytes(M, K)
     if workspace is None:
-        workspace = torch.empty(max(1, linear_w6ax_workspace_bytes(M, K)), dtype=torch.uint8,
-                                device=x.device)
-    ws_ptr = workspace.data_ptr()
-    ws_bytes = workspace.numel() * workspace.element_size()
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+    if isinstance(workspace, torch.Tensor) and workspace.dim() != 1:
+        raise ValueError(f"workspace must be 1-D, got shape {tuple(workspace.shape)}")
+    _tensor(workspace, torch.uint8, "workspace", min_bytes=need)
+    _on_gpu(x=x, w_packed=w_packed, s_w=s_w, y=y, workspace=workspace)
     _check(lib().flexq_linear_w6ax(x.data_ptr(), w_packed.data_ptr(), s_w.data_ptr(), M, N, K,
-                                   GROUP, abits, ws_ptr, ws_bytes, y.data_ptr(), _stream(x)),
-           "flexq_linear_w6ax")
+                                   GROUP, abits, workspace.data_ptr(), workspace.numel(),
+                                   y.data_ptr(), _stream(x)), "flexq_linear_w6ax")
     return y
 
 
 def gemm_w6ax_group_dots(q_a: torch.Tensor, w_packed: torch.Tensor, N: int,
                          dots: torch.Tensor | None = None):
     """int32 d[M][N][K/128] through the production unpack + int8 MFMA."""
-    _cuda(q_a, torch.int8, "q_a")
+    _matrix(q_a, torch.int8, "q_a")
     M, K = q_a.shape
+    G = _groups(K, "gemm_w6ax_group_dots")
+    N = _cols(N)
+    dev = q_a.device
+    _packed(w_packed, N, K)
     if dots is None:
-        dots = torch.empty((M, N, K // GROUP), dtype=torch.int32, device=q_a.device)
+        dots = torch.empty((M, N, G), dtype=torch.int32, device=dev)
+    _tensor(dots, torch.int32, "dots", shape=(M, N, G))
+    _on_gpu(q_a=q_a, w_packed=w_packed, dots=dots)
     _check(lib().flexq_gemm_w6ax_group_dots(q_a.data_ptr(), w_packed.data_ptr(), M, N, K, GROUP,
                                             dots.data_ptr(), _stream(q_a)),
            "flexq_gemm_w6ax_group_dots")
