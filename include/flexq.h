@@ -6,9 +6,9 @@
  *   - abstract: uniform 6-bit weights in every layer; activations kept at 6 bits
  *     in most layers and at 8 bits in sensitive ones; a kernel for the W6A6 and
  *     W6A8 matrix multiply;
- *   - blog "Six-bit frontier", section "Fine-Grained Quantization and Layer
- *     Sensitivity": weights and activations are split into small groups that
- *     share one scale factor;
+ *   - blog "Meet FlexQ: A Six-Bit Quantization Breakthrough", section
+ *     "Fine-Grained Quantization and Layer Sensitivity": weights and activations
+ *     are split into small groups that share one scale factor;
  *   - same blog, section "Bridging Software and Hardware with BTC": the groups run
  *     along K (128 deep), every group yields an exact integer partial product, and
  *     the dequantization is fused into the GEMM.
@@ -69,7 +69,9 @@ typedef enum {
   FLEXQ_SUCCESS = 0,
   FLEXQ_ERROR_INVALID_VALUE = 1, /* null pointer, negative size, abits not 6/8, overlap */
   FLEXQ_ERROR_UNSUPPORTED = 2,   /* group_size != 128, K % 128 != 0, N % 16 != 0, misalignment */
-  FLEXQ_ERROR_LAUNCH = 3         /* the HIP runtime rejected a launch */
+  FLEXQ_ERROR_LAUNCH = 3         /* hipLaunchKernel rejected one of the call's launches (its
+                                    own status, never an earlier call's sticky error);
+                                    kernels the call enqueued before it may still run */
 } flexq_status;
 
 typedef enum {

@@ -310,3 +310,27 @@ def test_stream_argument_is_honoured(fq):
         y = fq.gemm_w6ax(d_qa, d_sa, d_wp, d_sw, N, 6)
     s.synchronize()
     assert np.array_equal(u16(y), oracle.gemm_packed(qa, sa, wp, sw, N).view(np.uint16))
+
+
+def test_stale_hip_error_does_not_fail_the_next_call(fq):
+    """An error an earlier HIP call left in the thread's last-error slot is not
+    reported as a failed launch: each call returns the status of its own launches
+    (flexq.h, FLEXQ_ERROR_LAUNCH).  Covers the two-launch prefill tail split too."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")    # the HIP runtime torch and libflexq share
+    hip.hipSetDevice.restype = ctypes.c_int
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    dev = torch.cuda.current_device()
+    for M, N, K, path in [(5, 256, 512, fq.PATH_DECODE), (130, 256, 512, fq.PATH_PREFILL),
+                          (1024, 10240, 256, fq.PATH_AUTO)]:
+        x, w = inputs(14, M, N, K)
+        qa, sa = oracle.quant_act(x, 8)
+        wp, sw = oracle.pack_w6(w)
+        args = (to_dev(qa), to_dev(gm(sa)), to_dev(wp.view(np.int32)), to_dev(gm(sw)))
+        torch.cuda.synchronize()
+        assert hip.hipSetDevice(1 << 20) != 0      # an invalid device: a sticky error
+        assert torch.cuda.current_device() == dev
+        y = fq.gemm_w6ax(*args, N, 8, path=path)   # raises FlexqError on a non-zero status
+        assert np.array_equal(u16(y), oracle.gemm_packed(qa, sa, wp, sw, N).view(np.uint16))
+    assert fq.prefill_main_cols(1024, 10240, 256) < 10240   # the AUTO case ran the split
+    hip.hipGetLastError()                         # leave the thread's error slot clear

@@ -345,10 +345,9 @@ static hipError_t launch_decode_c(const int8_t* qa, const float* sa, const uint3
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                   uint16_t* y, int64_t ntiles16, int64_t ntiles, int64_t items,
                                   int64_t per_wg, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_decode_kernel<MT, T, S, P, C>), dim3((unsigned)grid), dim3(64 * S), 0,
-                     stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, y, (int)ntiles16,
-                     (int)ntiles, (int)items, (int)per_wg);
-  return hipGetLastError();
+  return launch_kernel(gemm_decode_kernel<MT, T, S, P, C>, dim3((unsigned)grid), dim3(64 * S),
+                       stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, y, (int)ntiles16,
+                       (int)ntiles, (int)items, (int)per_wg);
 }
 
 template <int MT, int T, int S, int P, int CMAX>

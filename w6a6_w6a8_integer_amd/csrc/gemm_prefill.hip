@@ -349,7 +349,11 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   issue_dma(0, 0);
   issue_regs(min(1, glast), breg[1]);
   issue_dma(min(1, glast), C::STAGE_BYTES);
-  wait_vm_lgkm0<OPS_PER_GROUP>();  // group 0 landed
+  // Group 0 must have landed before its fill.  Wait for every load issued so far:
+  // the compiler may sink a load of group 1 below this point, so a count of group
+  // 1's loads would not cover all of group 0's; group 1 was issued right after
+  // group 0, so waiting for it too costs almost nothing.
+  wait_vm_lgkm0<0>();
   fill(0, breg[0]);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   barrier();
@@ -572,25 +576,24 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
 
 // Columns n0 .. n0 + N - 1 of a product whose Y and s_w rows are ldn columns apart.
 template <int BM, int BN>
-static void launch_prefill_t(const int8_t* qa, const float* sa, const uint32_t* wp,
-                             const uint16_t* sw, int64_t M, int64_t n0, int64_t N, int64_t K,
-                             int64_t ldn, uint16_t* y, hipStream_t stream) {
+static hipError_t launch_prefill_t(const int8_t* qa, const float* sa, const uint32_t* wp,
+                                   const uint16_t* sw, int64_t M, int64_t n0, int64_t N,
+                                   int64_t K, int64_t ldn, uint16_t* y, hipStream_t stream) {
   const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   const int GM = 4;
-  hipLaunchKernelGGL((gemm_prefill_kernel<BM, BN>), dim3((unsigned)(nbm * nbn)), dim3(BM * 2), 0,
-                     stream, qa, sa, wp + (n0 / 16) * 3 * K, sw + n0, (int)M, (int)N, (int)K,
-                     (int)ldn, GM, y + n0);
+  return launch_kernel(gemm_prefill_kernel<BM, BN>, dim3((unsigned)(nbm * nbn)), dim3(BM * 2),
+                       stream, qa, sa, wp + (n0 / 16) * 3 * K, sw + n0, (int)M, (int)N, (int)K,
+                       (int)ldn, GM, y + n0);
 }
 
-static void launch_tile(int tile, const int8_t* qa, const float* sa, const uint32_t* wp,
+static hipError_t launch_tile(int tile, const int8_t* qa, const float* sa, const uint32_t* wp,
                         const uint16_t* sw, int64_t M, int64_t n0, int64_t N, int64_t K,
                         int64_t ldn, uint16_t* y, hipStream_t stream) {
   if (tile == kTile256x128)
-    launch_prefill_t<256, 128>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
-  else if (tile == kTile128x128)
-    launch_prefill_t<128, 128>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
-  else
-    launch_prefill_t<128, 64>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
+    return launch_prefill_t<256, 128>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
+  if (tile == kTile128x128)
+    return launch_prefill_t<128, 128>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
+  return launch_prefill_t<128, 64>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
 }
 
 int prefill_tile(int64_t M, int64_t N) {
@@ -640,18 +643,14 @@ hipError_t launch_gemm_prefill(const int8_t* qa, const float* sa, const uint32_t
                                hipStream_t stream, int tile) {
   if (tile == kTileAuto) {
     const int64_t n_main = prefill_main_cols(M, N);
-    launch_tile(prefill_tile(M, N), qa, sa, wp, sw, M, 0, n_main, K, N, y, stream);
-    if (n_main < N) {
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      launch_tile(kTile128x64, qa, sa, wp, sw, M, n_main, N - n_main, K, N, y, stream);
-    }
-    return hipGetLastError();
+    const hipError_t e = launch_tile(prefill_tile(M, N), qa, sa, wp, sw, M, 0, n_main, K, N, y,
+                                     stream);
+    if (e != hipSuccess || n_main == N) return e;
+    return launch_tile(kTile128x64, qa, sa, wp, sw, M, n_main, N - n_main, K, N, y, stream);
   }
   if (tile != kTile256x128 && tile != kTile128x128 && tile != kTile128x64)
     return hipErrorInvalidValue;
-  launch_tile(tile, qa, sa, wp, sw, M, 0, N, K, N, y, stream);
-  return hipGetLastError();
+  return launch_tile(tile, qa, sa, wp, sw, M, 0, N, K, N, y, stream);
 }
 
 }  // namespace flexq

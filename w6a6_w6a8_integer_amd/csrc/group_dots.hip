@@ -50,9 +50,8 @@ __global__ __launch_bounds__(64) void group_dots_kernel(const int8_t* __restrict
 hipError_t launch_group_dots(const int8_t* qa, const uint32_t* wp, int64_t M, int64_t N,
                              int64_t K, int32_t* dots, hipStream_t stream) {
   dim3 grid((unsigned)(N / 16), (unsigned)((M + 15) / 16), (unsigned)(K / kGroup));
-  hipLaunchKernelGGL(group_dots_kernel, grid, dim3(64), 0, stream, qa, wp, (int)M, (int)N,
-                     (int)K, dots);
-  return hipGetLastError();
+  return launch_kernel(group_dots_kernel, grid, dim3(64), stream, qa, wp, (int)M, (int)N, (int)K,
+                       dots);
 }
 
 }  // namespace flexq

@@ -4,7 +4,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace flexq {
+
+// Enqueue `kernel` on `stream` and return the status of this launch alone: the
+// runtime's answer to hipLaunchKernel, not the thread's sticky last error (which an
+// earlier failed HIP call, the caller's included, may have left behind).  The
+// arguments are converted to the kernel's parameter types first.
+template <typename... Params, typename... Args>
+hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t stream,
+                         Args... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  std::tuple<Params...> values(static_cast<Params>(args)...);
+  void* ptrs[sizeof...(Params)];
+  std::apply([&ptrs](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, values);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, stream);
+}
 
 hipError_t launch_pack_w6(const uint16_t* w, int64_t N, int64_t K, uint32_t* wp, uint16_t* sw,
                           hipStream_t stream);

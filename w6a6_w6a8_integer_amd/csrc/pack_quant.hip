@@ -72,16 +72,13 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 hipError_t launch_pack_w6(const uint16_t* w, int64_t N, int64_t K, uint32_t* wp, uint16_t* sw,
                           hipStream_t stream) {
   dim3 grid((unsigned)(N / 16), (unsigned)(K / kGroup));
-  hipLaunchKernelGGL(pack_w6_kernel, grid, dim3(128), 0, stream, w, (int)N, (int)K, wp, sw);
-  return hipGetLastError();
+  return launch_kernel(pack_w6_kernel, grid, dim3(128), stream, w, (int)N, (int)K, wp, sw);
 }
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int qmax, int8_t* qa,
                             float* sa, hipStream_t stream) {
   dim3 grid((unsigned)M, (unsigned)((K + 2047) / 2048));
-  hipLaunchKernelGGL(quant_act_kernel, grid, dim3(256), 0, stream, x, (int)M, (int)K, qmax, qa,
-                     sa);
-  return hipGetLastError();
+  return launch_kernel(quant_act_kernel, grid, dim3(256), stream, x, (int)M, (int)K, qmax, qa, sa);
 }
 
 }  // namespace flexq
