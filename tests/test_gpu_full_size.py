@@ -1,21 +1,32 @@
 """GPU parity at the full LLaMA-2 layer sizes, through the same calls the benchmark
 times (flexq_pack_w6, flexq_quant_act, flexq_gemm_w6ax with the automatic
-decode/prefill choice).
+decode/prefill choice), against the CPU oracle on the same seeded inputs.
 
-The oracle cannot redo a 4096 x 57344 x 8192 product in a test, but every output
-depends only on its own token row and weight row: a sample of rows and 16-column
-tiles is quantized and multiplied by the oracle alone and compared bit for bit with
-the GPU's outputs at those positions, together with the GPU's activation codes and
-scales of the sampled rows and its packed weights and scales of the sampled tiles.
-At M = 1 the one-call layer (flexq_linear_w6ax) must also give the two-call result
-in full, bit for bit.
+Scope, for every layer of every workload:
 
-Shapes: the toy W6A6 layer, LLaMA-2-7B W6A6 (M 1/16/128), LLaMA-2-13B W6A8
-(M 1/64/512), LLaMA-2-70B in W6A6 and W6A8 (M 1/16/64/256/1024/4096), and the
-distinct GEMMs of the 80-layer 70B stack (decode M = 32 and prefill M = 2048 in
-both precisions; the stack repeats these four layer shapes), and one GPU's share of
-the 70B layers under 8-way tensor parallelism.
+* packed weights and weight scales: the whole tensor, bit for bit;
+* activation codes and activation scales at every token count: the whole tensor;
+* Y: the whole output for the toy layer, every LLaMA-2-7B shape and every shape
+  with M <= 64 (the decode kernel's range); at larger M every column of 4 rows
+  (first, last, two seeded) plus 4096 seeded (row, column) outputs spread over the
+  whole grid of prefill tiles;
+* the int32 group dots (flexq_gemm_w6ax_group_dots): a slab of 16 token rows x 64
+  weight rows (four 16-row tiles) x every group, at every token count.
+
+Y is compared bit for bit: both kernels keep the sequential ascending-group fp32
+order of the definition.  At M <= 64 the one-call layer (flexq_linear_w6ax) must
+also give the two-call result in full.
+
+Workloads: the toy W6A6 layer, LLaMA-2-7B W6A6 (M 1/16/128), LLaMA-2-13B W6A8
+(M 1/64/512), LLaMA-2-70B in W6A6 and W6A8 (M 1/16/64/256/1024/4096), the distinct
+GEMMs of the 80-layer 70B stack (decode M = 32 and prefill M = 2048 in both
+precisions; every layer of the stack holds the same four shapes and, in the
+benchmark, the same synthetic values), and one GPU's share of the 70B layers under
+8-way tensor parallelism.  The oracle's quantizers run over row blocks in parallel
+threads and its GEMM over column blocks, so each case finishes in seconds.
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
@@ -28,6 +39,8 @@ pytestmark = [pytest.mark.gpu,
 
 DEV = "cuda:0"
 G = 128
+FULL_Y_MAX_M = 64
+PAIRS = 4096
 
 STACK_70B = {"layers": synth.LLAMA2_70B, "M": (32, 2048), "abits": (6, 8)}
 # One GPU's share of the 70B layers under 8-way tensor parallelism (qkv and gate_up
@@ -36,10 +49,14 @@ TP8_70B = {"layers": {"qkv": (10240 // 8, 8192), "o": (8192, 8192 // 8),
                       "gate_up": (57344 // 8, 8192), "down": (8192, 28672 // 8)},
            "M": (1, 16, 64, 256, 1024, 4096), "abits": (6, 8)}
 EXTRA = {"llama2_70b_stack": STACK_70B, "llama2_70b_tp8_shard": TP8_70B}
+FULL_Y_WORKLOADS = {"toy_w6a6", "llama2_7b_w6a6"}
 CASES = []
 for wname, wl in list(synth.WORKLOADS.items()) + list(EXTRA.items()):
     for lname in wl["layers"]:
         CASES.append((wname, lname))
+
+THREADS = synth.default_threads()
+_pool = ThreadPoolExecutor(THREADS)
 
 
 @pytest.fixture(scope="module")
@@ -53,61 +70,137 @@ def say(*a):
     print(*a, flush=True)
 
 
-def sample_rows(M, rng):
-    rows = {0, M - 1, M // 2}
-    rows.update(int(r) for r in rng.integers(0, M, 3))
-    return np.array(sorted(rows))
+def _blocks(n, step=1):
+    """Split range(n) into up to 2 * THREADS blocks whose bounds are multiples of step."""
+    per = max(step, -(-n // (2 * THREADS) // step) * step)
+    return [(a, min(n, a + per)) for a in range(0, n, per)]
 
 
-def sample_tiles(N, rng):
-    tiles = {0, N // 16 - 1}
-    tiles.update(int(t) for t in rng.integers(0, N // 16, 2))
-    return np.array(sorted(tiles))
+def oracle_quant_w6(w):
+    N, K = w.shape
+    qw = np.empty((N, K), np.int8)
+    sw = np.empty((N, K // G), np.float16)
+
+    def job(ab):
+        a, b = ab
+        qw[a:b], sw[a:b] = oracle.quant_w6(w[a:b])
+    list(_pool.map(job, _blocks(N)))
+    return qw, sw
+
+
+def oracle_pack_codes(qw):
+    N, K = qw.shape
+    wp = np.empty(3 * N * K // 16, np.uint32)
+
+    def job(ab):   # rows a..b are 16-row tiles a/16..b/16, a contiguous run of words
+        a, b = ab
+        wp[3 * a * K // 16:3 * b * K // 16] = oracle.pack_codes(qw[a:b])
+    list(_pool.map(job, _blocks(N, 16)))
+    return wp
+
+
+def oracle_quant_act(x, abits):
+    M, K = x.shape
+    qa = np.empty((M, K), np.int8)
+    sa = np.empty((M, K // G), np.float32)
+
+    def job(ab):
+        a, b = ab
+        qa[a:b], sa[a:b] = oracle.quant_act(x[a:b], abits)
+    list(_pool.map(job, _blocks(M)))
+    return qa, sa
+
+
+def first_diffs(got, ref, index):
+    bad = np.argwhere(got != ref)
+    return f"{len(bad)} of {got.size} differ, first at {[index(b) for b in bad[:4]]}"
 
 
 @pytest.mark.parametrize("wname,lname", CASES, ids=[f"{w}-{l}" for w, l in CASES])
-def test_full_size_sampled(fq, wname, lname):
+def test_full_size(fq, wname, lname):
     wl = EXTRA[wname] if wname in EXTRA else synth.WORKLOADS[wname]
     N, K = wl["layers"][lname]
     seed = synth.derive_seed(synth.BASE_SEED, "full", wname, lname)
     rng = np.random.default_rng(seed & 0xFFFFFFFF)
-    w = synth.weights(synth.derive_seed(seed, "w"), N, K, nthreads=synth.default_threads())
+    say(f"{wname} {lname}: N={N} K={K}: pack_w6")
+    w = synth.weights(synth.derive_seed(seed, "w"), N, K, nthreads=THREADS)
     wp, sw = fq.pack_w6(torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
 
-    tiles = sample_tiles(N, rng)
-    cols = np.concatenate([np.arange(16 * t, 16 * t + 16) for t in tiles])
-    wp_all = wp.cpu().numpy().view(np.uint32)
-    sw_all = sw.cpu().numpy().view(np.uint16)          # [K/128][N]
-    # the sampled tiles' packed words and scales against the oracle's packing
-    w_s = np.ascontiguousarray(w[cols])
-    wp_ref, sw_ref = oracle.pack_w6(w_s)                # tiles in sampled order
-    words = 3 * K                                       # one 16-row tile
-    for i, t in enumerate(tiles):
-        assert np.array_equal(wp_all[t * words:(t + 1) * words], wp_ref[i * words:(i + 1) * words]), \
-            f"packed tile {t}"
-    assert np.array_equal(sw_all[:, cols].T, sw_ref.view(np.uint16))
-    qw_ref, _ = oracle.quant_w6(w_s)
+    # packed weights and weight scales, whole tensors
+    qw, sw_ref = oracle_quant_w6(w)
     del w
+    wp_ref = oracle_pack_codes(qw)
+    wp_got = wp.cpu().numpy().view(np.uint32)[:wp_ref.size]
+    assert np.array_equal(wp_got, wp_ref), first_diffs(
+        wp_got, wp_ref, lambda b: f"dword {int(b[0])} (tile {int(b[0]) // (3 * K)})")
+    sw_got = sw.cpu().numpy().view(np.uint16).T          # group-major -> [N][G]
+    assert np.array_equal(sw_got, sw_ref.view(np.uint16)), first_diffs(
+        sw_got, sw_ref.view(np.uint16), lambda b: (int(b[0]), int(b[1])))
+    del wp_got, wp_ref
 
     for M in wl["M"]:
-        x = synth.activations(synth.derive_seed(seed, "x", M), M, K, nthreads=synth.default_threads())
+        x = synth.activations(synth.derive_seed(seed, "x", M), M, K, nthreads=THREADS)
         xd = torch.from_numpy(x).to(DEV)
-        rows = sample_rows(M, rng)
         for abits in wl["abits"]:
-            say(f"{wname} {lname} M={M} N={N} K={K} abits={abits}")
+            say(f"{wname} {lname}: M={M} N={N} K={K} abits={abits}")
             qa, sa = fq.quant_act(xd, abits)
             y = fq.gemm_w6ax(qa, sa, wp, sw, N, abits)
-            if M == 1:
-                y_lin = fq.linear_w6ax(xd, wp, sw, N, abits)
-                assert torch.equal(y_lin.view(torch.int16), y.view(torch.int16))
             torch.cuda.synchronize()
-            qa_ref, sa_ref = oracle.quant_act(np.ascontiguousarray(x[rows]), abits)
-            assert np.array_equal(qa[torch.from_numpy(rows).to(DEV)].cpu().numpy(), qa_ref)
-            assert np.array_equal(sa.cpu().numpy()[:, rows].T.view(np.uint32),
-                                  sa_ref.view(np.uint32))
-            y_ref = oracle.gemm(qa_ref, sa_ref, qw_ref, sw_ref)
-            got = y.cpu().numpy()[np.ix_(rows, cols)].view(np.uint16)
-            bad = np.argwhere(got != y_ref.view(np.uint16))
-            assert bad.size == 0, f"{len(bad)} of {got.size} sampled outputs differ, first " \
-                                  f"(row, col) {[(int(rows[i]), int(cols[j])) for i, j in bad[:4]]}"
+
+            # activation codes and scales, whole tensors
+            qa_ref, sa_ref = oracle_quant_act(x, abits)
+            qa_got = qa.cpu().numpy()
+            assert np.array_equal(qa_got, qa_ref), first_diffs(
+                qa_got, qa_ref, lambda b: (int(b[0]), int(b[1])))
+            sa_got = sa.cpu().numpy().T.view(np.uint32)
+            assert np.array_equal(sa_got, sa_ref.view(np.uint32)), first_diffs(
+                sa_got, sa_ref.view(np.uint32), lambda b: (int(b[0]), int(b[1])))
+            del qa_got, sa_got
+
+            # group dots: 16 token rows x 64 weight rows x every group
+            rows16 = np.sort(rng.choice(M, min(M, 16), replace=False))
+            t0 = int(rng.integers(0, max(1, N // 16 - 3)))
+            nt = min(4, N // 16 - t0)
+            dots = fq.gemm_w6ax_group_dots(
+                qa[torch.from_numpy(rows16).to(DEV)].contiguous(),
+                wp[3 * K * t0:3 * K * (t0 + nt)], 16 * nt)
+            torch.cuda.synchronize()
+            d_ref = oracle.group_dots(np.ascontiguousarray(qa_ref[rows16]),
+                                      np.ascontiguousarray(qw[16 * t0:16 * (t0 + nt)]),
+                                      nthreads=THREADS)
+            d_got = dots.cpu().numpy()
+            assert np.array_equal(d_got, d_ref), first_diffs(
+                d_got, d_ref, lambda b: (int(rows16[b[0]]), 16 * t0 + int(b[1]), int(b[2])))
+
+            # Y
+            if M <= FULL_Y_MAX_M or wname in FULL_Y_WORKLOADS:
+                y_ref = oracle.gemm(qa_ref, sa_ref, qw, sw_ref, nthreads=THREADS)
+                y_got = y.cpu().numpy().view(np.uint16)
+                assert np.array_equal(y_got, y_ref.view(np.uint16)), first_diffs(
+                    y_got, y_ref.view(np.uint16), lambda b: (int(b[0]), int(b[1])))
+                if M <= FULL_Y_MAX_M:
+                    y_lin = fq.linear_w6ax(xd, wp, sw, N, abits)
+                    assert torch.equal(y_lin.view(torch.int16), y.view(torch.int16))
+            else:
+                rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 2)]))
+                y_ref = oracle.gemm(np.ascontiguousarray(qa_ref[rows]),
+                                    np.ascontiguousarray(sa_ref[rows]), qw, sw_ref,
+                                    nthreads=THREADS)
+                y_got = y[torch.from_numpy(rows).to(DEV)].cpu().numpy().view(np.uint16)
+                assert np.array_equal(y_got, y_ref.view(np.uint16)), first_diffs(
+                    y_got, y_ref.view(np.uint16), lambda b: (int(rows[b[0]]), int(b[1])))
+                pm = rng.integers(0, M, PAIRS)
+                pn = rng.integers(0, N, PAIRS)
+                got = y[torch.from_numpy(pm).to(DEV), torch.from_numpy(pn).to(DEV)]
+                got = got.cpu().numpy().view(np.uint16)
+
+                def one(i):
+                    m, n = int(pm[i]), int(pn[i])
+                    return oracle.gemm(qa_ref[m:m + 1], sa_ref[m:m + 1], qw[n:n + 1],
+                                       sw_ref[n:n + 1], nthreads=1).view(np.uint16)[0, 0]
+                ref = np.array(list(_pool.map(one, range(PAIRS))), np.uint16)
+                assert np.array_equal(got, ref), first_diffs(
+                    got, ref, lambda b: (int(pm[b[0]]), int(pn[b[0]])))
+            del y
         del xd
