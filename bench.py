@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--seed", type=int, default=synth.BASE_SEED)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-peaks", action="store_true",
+                   help="skip the on-device peak measurements (HBM read, MFMA loop)")
     p.add_argument("--eager", action="store_true",
                    help="time the step launch by launch only (no HIP graph replay)")
     p.add_argument("--cpu-sample-cols", type=int, default=512,
@@ -147,15 +149,16 @@ def main():
     a8_layers = set(np.random.default_rng(synth.derive_seed(args.seed, "stack-a8") & 0xFFFFFFFF)
                     .choice(STACK_LAYERS, STACK_A8_LAYERS, replace=False).tolist()) if stack else set()
 
-    # ---- weights: generated on the host, packed on the GPU, resident copies rotated
-    # between launches so that no layer is served from the 256 MB MALL (at least two
-    # copies and at least 1 GiB of packed weights in all)
+    # ---- weights: generated on the host, packed on the GPU.  Resident copies are
+    # rotated so that no layer is served from the 256 MB MALL: every (M, abits) block
+    # of the step (one launch per linear layer) reads copy `block % ncopies`, so
+    # consecutive blocks read different copies and a copy is read again only after
+    # min(ncopies, blocks per step) - 1 other blocks, i.e. at least one other whole
+    # layer set (641.7 MB for the 70B layers) has streamed through.
     t0 = time.time()
     packed = {}
     set_bytes = sum(0.75 * N * K for N, K in LAYERS.values())
     ncopies = max(2, -(-(1 << 30) // int(set_bytes)))
-    if (len(m_list) * len(ABITS) * len(LAYERS)) % ncopies == 0 and ncopies > 2:
-        ncopies += 1  # a step's launch i then meets a different copy in every step
     if stack:
         ncopies = STACK_LAYERS  # one resident copy per decoder layer (same synthetic values)
     for li, (name, (N, K)) in enumerate(LAYERS.items()):
@@ -187,23 +190,23 @@ def main():
     # Largest M first: while the long prefill launches run, the host queues the rest of
     # the step, so the short decode launches at the end start back to back and their
     # events time the GPU, not the host's launch path.
-    # Each launch: (M, abits, linear, weight copy or None = rotate through the copies).
+    # Each launch: (M, abits, linear, weight copy).
     if stack:
         plan = [(M, 8 if layer in a8_layers else 6, name, layer)
                 for M in sorted(m_list, reverse=True) for layer in range(STACK_LAYERS)
                 for name in LAYERS]
     else:
-        plan = [(M, ab, name, None) for M in sorted(m_list, reverse=True) for ab in ABITS
-                for name in LAYERS]
+        blocks = [(M, ab) for M in sorted(m_list, reverse=True) for ab in ABITS]
+        plan = [(M, ab, name, b % ncopies) for b, (M, ab) in enumerate(blocks) for name in LAYERS]
     keys = sorted({e[:3] for e in plan}, key=lambda k: (-k[0], k[1], list(LAYERS).index(k[2])))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in plan]
 
-    def step(timed: bool, s: int):
+    def step(timed: bool):
         for i, (M, ab, name, widx) in enumerate(plan):
             N, K = LAYERS[name]
             _, xd, qa, sa, y = bufs[(M, name)]
-            wp, sw = packed[name][widx if widx is not None else (s * len(plan) + i) % ncopies]
+            wp, sw = packed[name][widx]
             if timed:
                 ev[i][0].record()
             fq.quant_act(xd, ab, q_a=qa, s_a=sa)
@@ -214,39 +217,42 @@ def main():
                 ev[i][2].record()
 
     for s in range(args.warmup):
-        step(False, s)
+        step(False)
     torch.cuda.synchronize()
 
     quant_ms = {k: [] for k in keys}
     gemm_ms = {k: [] for k in keys}
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     step_ms = []
+    # Per-kernel times come from events around every launch of the eager steps.  A
+    # busy kernel (about 10 ms of MFMA work) holds the GPU before each such step, so
+    # the host has queued the whole step -- every launch and event -- before the GPU
+    # reaches it: the events then time the kernels back to back, not the host's
+    # launch path.
+    sink = torch.empty(fq.peak_sink_bytes(), dtype=torch.uint8, device=dev)
+    clock = torch.zeros(2, dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     wall0 = time.time()
-    start.record()
     for s in range(args.steps):
-        step(True, s)
-        torch.cuda.synchronize()  # read this step's events; the region stays back to back
+        fq.peak_mfma_i8(80000, 0, sink, clock)
+        step(True)
+        torch.cuda.synchronize()  # read this step's events
         for i, e in enumerate(plan):
             quant_ms[e[:3]].append(ev[i][0].elapsed_time(ev[i][1]))
             gemm_ms[e[:3]].append(ev[i][1].elapsed_time(ev[i][2]))
         step_ms.append(ev[0][0].elapsed_time(ev[-1][2]))
-    stop.record()
-    torch.cuda.synchronize()
     wall = time.time() - wall0
-    total_ms = start.elapsed_time(stop)
+    total_ms = sum(step_ms)
     ms_per_step_eager = statistics.median(step_ms)
 
-    # The same step captured once as a HIP graph and replayed: the kernels and their
-    # arguments are the eager step's (launch i reading weight copy i % ncopies), only
-    # the host-side launch gaps between the kernels go.  Per-kernel figures above come
-    # from the eager steps' events.
+    # The same step captured once as a HIP graph and replayed back to back: the kernels
+    # and their arguments are the eager step's (the same weight copies); ms_per_step
+    # and value come from these replays.
     graph_ms = None
     if not args.eager:
         try:
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
-                step(False, 0)
+                step(False)
             graph.replay()
             torch.cuda.synchronize()
         except RuntimeError as e:  # capture unsupported here: report the eager time
@@ -264,112 +270,202 @@ def main():
             wall += time.time() - wall1
             graph_ms = [e0.elapsed_time(e1) for e0, e1 in gev]
             total_ms += gev[0][0].elapsed_time(gev[-1][1])
+            torch.cuda.synchronize()
 
     # ---- aggregate
+    keys_by_m = sorted(keys, key=lambda k: (k[0], k[1], list(LAYERS).index(k[2])))
+    kernel_of = {k: ("decode" if fq.auto_path(k[0], *LAYERS[k[2]]) == fq.PATH_DECODE
+                     else "prefill") for k in keys}
+    tot_ops = sum(2.0 * e[0] * LAYERS[e[2]][0] * LAYERS[e[2]][1] for e in plan)
+    per_step = {k: len(gemm_ms[k]) // len(step_ms) for k in keys}
+
+    def pct(v, q):
+        v = sorted(v)
+        return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+
+    # on-device measured peaks (include/flexq_peaks.h), after the timed region
+    peaks = None if args.no_peaks else measure_peaks(fq, torch, dev, LAYERS)
+
     shapes = []
-    tot_ops = 0.0
-    dec_ops = dec_bytes = dec_ms = 0.0
-    pre_ops = pre_ms = 0.0
-    for e in plan:
-        tot_ops += 2.0 * e[0] * LAYERS[e[2]][0] * LAYERS[e[2]][1]
-    for k in keys:
+    for k in keys_by_m:
         M, ab, name = k
         N, K = LAYERS[name]
         g = statistics.median(gemm_ms[k])
-        q = statistics.median(quant_ms[k])
         ops = 2.0 * M * N * K
         by = gemm_bytes(M, N, K)
-        gsum = sum(gemm_ms[k])
-        if fq.auto_path(M, N, K) == fq.PATH_DECODE:
-            dec_ops += ops * len(gemm_ms[k])
-            dec_bytes += by * len(gemm_ms[k])
-            dec_ms += gsum
-        else:
-            pre_ops += ops * len(gemm_ms[k])
-            pre_ms += gsum
-        shapes.append({
-            "layer": name, "M": M, "N": N, "K": K, "abits": ab,
-            "kernel": "decode" if fq.auto_path(M, N, K) == fq.PATH_DECODE else "prefill",
-            "tile": (None if fq.auto_path(M, N, K) == fq.PATH_DECODE else
-                     TILE_NAMES[fq.prefill_tile(M, N, K)]),
-            # columns a second prefill launch of 128 x 64 tiles covers (tail split)
-            "tail_cols": (N - fq.prefill_main_cols(M, N, K)
-                          if fq.auto_path(M, N, K) == fq.PATH_PREFILL else 0),
-            "gemm_us": round(g * 1e3, 2), "quant_us": round(q * 1e3, 2),
-            "tops": round(ops / (g * 1e-3) / 1e12, 2),
-            "gbs": round(by / (g * 1e-3) / 1e9, 1),
-            "frac_hbm": round(by / (g * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
-            "frac_int8": round(ops / (g * 1e-3) / 1e12 / INT8_PEAK_TOPS, 3),
-            "quant_gbs": round(quant_bytes(M, K) / (q * 1e-3) / 1e9, 1),
-            "launches_per_step": len(gemm_ms[k]) // len(step_ms),
-        })
-    shapes.sort(key=lambda r: (r["M"], r["abits"], list(LAYERS).index(r["layer"])))
-    ms_per_step = statistics.median(graph_ms) if graph_ms else ms_per_step_eager
-    value = tot_ops / (ms_per_step * 1e-3) / 1e12
+        dec = kernel_of[k] == "decode"
+        row = [name, M, ab, "decode" if dec else TILE_NAMES[fq.prefill_tile(M, N, K)]
+               + ("+128x64" if fq.prefill_main_cols(M, N, K) < N else ""),
+               round(g * 1e3, 2), round(pct(gemm_ms[k], 0.1) * 1e3, 2),
+               round(pct(gemm_ms[k], 0.9) * 1e3, 2), round(statistics.median(quant_ms[k]) * 1e3, 2),
+               round(ops / (g * 1e-3) / 1e12, 1), round(by / (g * 1e-3) / 1e9, 1),
+               round(by / (g * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+               round(ops / (g * 1e-3) / 1e12 / INT8_PEAK_TOPS, 3)]
+        if peaks:
+            # against what this GPU measurably reaches: a plain read of the layer's
+            # weight bytes, or the back-to-back MFMA loop
+            row.append(round(by / (g * 1e-3) / 1e9 / peaks["hbm_read_gbs"][name], 3) if dec
+                       else round(ops / (g * 1e-3) / 1e12 / peaks["mfma_i8_tops"], 3))
+        shapes.append(row)
+    shape_cols = ["layer", "M", "abits", "kernel", "gemm_us_median", "gemm_us_p10",
+                  "gemm_us_p90", "quant_us_median", "tops", "gbs", "frac_hbm_8tbs",
+                  "frac_int8_5pops"] + (["frac_measured_peak"] if peaks else [])
 
-    pre_tops = pre_ops / (pre_ms * 1e-3) / 1e12 if pre_ms else 0.0
-    # a prefill GEMM call is one kernel launch, two when the tail split applies
-    pre_launches = sum(1 for (M, _, name, _) in plan
-                       if fq.auto_path(M, *LAYERS[name]) == fq.PATH_PREFILL)
-    pre_kernels = sum(1 + (fq.prefill_main_cols(M, *LAYERS[name]) < LAYERS[name][0])
-                      for (M, _, name, _) in plan
-                      if fq.auto_path(M, *LAYERS[name]) == fq.PATH_PREFILL)
-    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9 if dec_ms else 0.0
-    if pre_ms >= dec_ms:
-        # integer ops: the unit is TOP/s against the dense int8 MFMA peak
-        roofline = {"kernel": "gemm_prefill_kernel", "bound": "mfma", "achieved": round(pre_tops, 1),
-                    "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": round(pre_tops / INT8_PEAK_TOPS, 4),
+    def over(sel, kern):
+        """Summed algorithmic bytes / ops over summed event times of the selected GEMMs."""
+        ks = [k for k in keys if sel(k[0]) and kernel_of[k] == kern]
+        ms = sum(sum(gemm_ms[k]) for k in ks)
+        if not ms:
+            return None
+        byt = sum(gemm_bytes(k[0], *LAYERS[k[2]]) * len(gemm_ms[k]) for k in ks)
+        ops = sum(2.0 * k[0] * LAYERS[k[2]][0] * LAYERS[k[2]][1] * len(gemm_ms[k]) for k in ks)
+        r = {"gbs": byt / (ms * 1e-3) / 1e9, "tops": ops / (ms * 1e-3) / 1e12, "ms": ms}
+        if peaks:
+            # time each launch would take at the plain-read rate of its layer's size
+            ideal = sum(gemm_bytes(k[0], *LAYERS[k[2]]) / (peaks["hbm_read_gbs"][k[2]] * 1e9)
+                        * len(gemm_ms[k]) for k in ks)
+            r["hbm_frac_measured"] = ideal / (ms * 1e-3)
+        return r
+
+    dec_all = over(lambda M: True, "decode")
+    pre_all = over(lambda M: True, "prefill")
+    dec16 = over(lambda M: M <= 16, "decode")
+    pre1024 = over(lambda M: M >= 1024, "prefill")
+    targets = {
+        "hbm_frac_m_le_16": round(dec16["gbs"] / HBM_PEAK_GBS, 4) if dec16 else None,
+        "hbm_frac_m_le_16_goal": 0.70,
+        "int8_frac_m_ge_1024": round(pre1024["tops"] / INT8_PEAK_TOPS, 4) if pre1024 else None,
+        "int8_frac_m_ge_1024_goal": 0.50,
+    }
+    if peaks and dec16:
+        targets["hbm_frac_m_le_16_of_measured_read"] = round(dec16["hbm_frac_measured"], 4)
+    if peaks and pre1024:
+        targets["int8_frac_m_ge_1024_of_measured_mfma"] = round(
+            pre1024["tops"] / peaks["mfma_i8_tops"], 4)
+
+    pre_launches = sum(per_step[k] for k in keys if kernel_of[k] == "prefill")
+    pre_kernels = sum(per_step[k] * (1 + (fq.prefill_main_cols(k[0], *LAYERS[k[2]]) <
+                                          LAYERS[k[2]][0]))
+                      for k in keys if kernel_of[k] == "prefill")
+    if pre_all and (not dec_all or pre_all["ms"] >= dec_all["ms"]):
+        roofline = {"kernel": "gemm_prefill_kernel", "bound": "mfma",
+                    "achieved": round(pre_all["tops"], 1), "peak": INT8_PEAK_TOPS,
+                    "unit": "TOP/s", "frac": round(pre_all["tops"] / INT8_PEAK_TOPS, 4),
                     # counters were taken on the default workload's launches only
                     "traffic": (recorded_traffic() if args.layers == "70b" and not args.m
                                 else None),
-                    "launches_per_step": pre_launches,
-                    "kernel_launches_per_step": pre_kernels,
-                    "ops_per_launch": round(pre_ops / len(step_ms) / max(pre_launches, 1))}
+                    "timing": "HIP events around each launch on its stream, all steps",
+                    "launches_per_step": pre_launches, "kernel_launches_per_step": pre_kernels,
+                    "ops_per_launch": round(sum(2.0 * k[0] * LAYERS[k[2]][0] * LAYERS[k[2]][1]
+                                                * per_step[k] for k in keys
+                                                if kernel_of[k] == "prefill") / max(pre_launches, 1))}
+        if peaks:
+            roofline["measured_peak"] = round(peaks["mfma_i8_tops"], 1)
+            roofline["frac_of_measured_peak"] = round(pre_all["tops"] / peaks["mfma_i8_tops"], 4)
     else:
-        roofline = {"kernel": "gemm_decode_kernel", "bound": "hbm", "achieved": round(dec_gbs, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": None}
-    roofline_decode = {"kernel": "gemm_decode_kernel", "bound": "hbm", "achieved": round(dec_gbs, 1),
-                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
+        roofline = {"kernel": "gemm_decode_kernel", "bound": "hbm",
+                    "achieved": round(dec_all["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(dec_all["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                    "timing": "HIP events around each launch on its stream, all steps"}
+    # the two target figures also as scalars of the roofline record
+    roofline["hbm_frac_m_le_16"] = targets["hbm_frac_m_le_16"]
+    roofline["int8_frac_m_ge_1024"] = targets["int8_frac_m_ge_1024"]
+    roofline_decode = None
+    if dec_all:
+        roofline_decode = {"kernel": "gemm_decode_kernel", "bound": "hbm",
+                           "achieved": round(dec_all["gbs"], 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(dec_all["gbs"] / HBM_PEAK_GBS, 4)}
+        if peaks:
+            roofline_decode["frac_of_measured_read"] = round(dec_all["hbm_frac_measured"], 4)
 
-    # the two target rows: HBM fraction over the M <= 16 GEMMs, int8 MFMA fraction over
-    # the M >= 1024 GEMMs (algorithmic bytes / ops over summed event times)
-    def frac_over(sel, num, peak, scale):
-        ks = [k for k in keys if sel(k[0])]
-        tot = sum(num(k) * len(gemm_ms[k]) for k in ks)
-        ms = sum(sum(gemm_ms[k]) for k in ks)
-        return round(tot / (ms * 1e-3) / scale / peak, 4) if ms else None
-    targets = {
-        "hbm_frac_m_le_16": frac_over(lambda M: M <= 16,
-                                      lambda k: gemm_bytes(k[0], *LAYERS[k[2]]), HBM_PEAK_GBS, 1e9),
-        "int8_frac_m_ge_1024": frac_over(lambda M: M >= 1024,
-                                         lambda k: 2.0 * k[0] * LAYERS[k[2]][0] * LAYERS[k[2]][1],
-                                         INT8_PEAK_TOPS, 1e12),
-    }
+    ms_per_step = statistics.median(graph_ms) if graph_ms else ms_per_step_eager
+    value = tot_ops / (ms_per_step * 1e-3) / 1e12
 
     cpu = None
     if not args.no_cpu_baseline:
-        per_step = {k: len(gemm_ms[k]) // len(step_ms) for k in keys}
         cpu = cpu_baseline(bufs, per_step, args.cpu_sample_cols, packed, ms_per_step, tot_ops)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
-        "launch": "hip_graph" if graph_ms else "eager",
-        "ms_per_step_eager": round(ms_per_step_eager, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.layers], "weight_copies": ncopies,
                    **({"stack_layers": STACK_LAYERS, "a8_layers": sorted(a8_layers)} if stack else {}),
                    "layers": {k: list(v) for k, v in LAYERS.items()}, "M": list(m_list),
                    "abits": list(ABITS), "group": GROUP, "step": "quant_act + gemm per (M, abits, layer)"},
-        "roofline": roofline, "roofline_decode": roofline_decode, "targets": targets,
-        "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu,
+        "launch": "hip_graph" if graph_ms else "eager",
+        "ms_per_step_eager": round(ms_per_step_eager, 3),
+        "ms_per_step_p10_p90": ([round(pct(graph_ms, 0.1), 3), round(pct(graph_ms, 0.9), 3)]
+                                if graph_ms else [round(pct(step_ms, 0.1), 3),
+                                                  round(pct(step_ms, 0.9), 3)]),
         "timed_region_ms": round(total_ms, 2), "wall_s": round(wall, 2),
-        "shapes": shapes,
+        "shape_cols": shape_cols, "shapes": shapes,
+        # last, where a truncated tail of the line still shows them
+        "peaks": peaks, "roofline_decode": roofline_decode, "targets": targets,
     }
-    print(json.dumps(out), flush=True)
+    print(json.dumps(out, separators=(",", ":")), flush=True)
+
+
+def measure_peaks(fq, torch, dev, layers):
+    """What this GPU reaches with the simplest kernels (include/flexq_peaks.h):
+    a plain non-temporal read of each layer's packed-weight byte count and of 1 GiB
+    (rotating over 3 buffers so no read is served from the MALL), and back-to-back
+    int8 MFMAs with 0 and 8 independent FMAs per MFMA (8 = the fused rescale's count),
+    with the shader clock of the MFMA loop.  Medians of several launches."""
+    sink = torch.empty(fq.peak_sink_bytes(), dtype=torch.uint8, device=dev)
+    clock = torch.zeros(2, dtype=torch.int64, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        """Median event time of fn's launch.  A busy kernel (about 50 us) runs first
+        each time, so the host has enqueued the start event, the launch and the end
+        event before the GPU reaches them: the interval holds the kernel alone, not
+        the host's launch latency."""
+        fn()
+        ts = []
+        for _ in range(reps):
+            fq.peak_mfma_i8(400, 0, sink, clock)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    out = {"hbm_read_gbs": {}}
+    bufs = [torch.empty(1 << 30, dtype=torch.uint8, device=dev) for _ in range(3)]
+    for b in bufs:
+        b.fill_(1)
+    sizes = {name: int(gemm_bytes(1, N, K)) // 16 * 16 for name, (N, K) in layers.items()}
+    sizes["1GiB"] = 1 << 30
+    for name, n in sizes.items():
+        it = iter(range(1 << 30))
+        ms = timed(lambda: fq.peak_hbm_read(bufs[next(it) % 3][:n], sink), 9)
+        out["hbm_read_gbs"][name] = round(n / (ms * 1e-3) / 1e9, 1)
+    del bufs
+    for v, key in ((0, "mfma_i8"), (8, "mfma_i8_valu8")):
+        iters = 4000
+        ops = fq.peak_mfma_i8(iters, v, sink, clock)
+        ms = timed(lambda: fq.peak_mfma_i8(iters, v, sink, clock), 5)
+        c = clock.cpu().tolist()
+        out[key + "_tops"] = round(ops / (ms * 1e-3) / 1e12, 1)
+        out[key + "_clock_ghz"] = round(c[0] / c[1] * 0.1, 3)
+    out["mfma_i8_valu8_frac_of_5pops"] = round(out["mfma_i8_valu8_tops"] / INT8_PEAK_TOPS, 4)
+    props = torch.cuda.get_device_properties(dev)
+    out["device"] = getattr(props, "gcnArchName", props.name)
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(bufs, per_step, cols, packed, gpu_ms_per_step, tot_ops):
@@ -377,15 +473,17 @@ def cpu_baseline(bufs, per_step, cols, packed, gpu_ms_per_step, tot_ops):
     (M, abits, layer) of the step, the full activation quantization, and the GEMM
     restricted to its first `cols` output columns; the GEMM time is scaled linearly
     in N (exact: the work is linear in N) and each shape's time by the number of
-    times a step runs it, to estimate the oracle's time for the whole step."""
+    times a step runs it, to estimate the oracle's time for the whole step.  The GEMM
+    runs on synth.default_threads() threads (the host cores this process may use,
+    at most 16: the CPU share of one GPU on the benchmark's machines); two
+    single-thread figures are added: the toy 16 x 256 x 512 layer and the 70B down
+    projection at M = 1."""
     import oracle
-    import torch
 
     threads = synth.default_threads()
     q_time = 0.0
     g_time = 0.0
     g_time_scaled = 0.0
-    sample_ops = 0.0
     wq = {}
     for name, (N, K) in LAYERS.items():
         wp, sw = packed[name][0]
@@ -408,15 +506,28 @@ def cpu_baseline(bufs, per_step, cols, packed, gpu_ms_per_step, tot_ops):
         dt = time.perf_counter() - t
         g_time += dt
         g_time_scaled += dt * (N / n) * count
-        sample_ops += 2.0 * M * n * K
     est_step_s = q_time_step + g_time_scaled
+
+    def single(M, N, K, seed):
+        x = synth.activations(synth.derive_seed(seed, "x"), M, K)
+        w = synth.weights(synth.derive_seed(seed, "w"), N, K)
+        qa, sa = oracle.quant_act(x, 6)
+        qw, sw = oracle.quant_w6(w)
+        t = time.perf_counter()
+        oracle.gemm(qa, sa, qw, sw, nthreads=1)
+        return round(2.0 * M * N * K / (time.perf_counter() - t) / 1e9, 3)
+
     return {"value": round(tot_ops / est_step_s / 1e12, 5), "unit": "TOPS", "cores": threads,
             "kind": "oracle",
-            "sample": (f"every distinct (M, abits, layer) of the step: full activation quantization "
-                       f"({q_time:.1f} s, 1 thread) and the GEMM on the first {cols} output "
-                       f"columns ({g_time:.1f} s, {threads} threads), GEMM time scaled by N/{cols}; "
-                       f"estimated oracle step {est_step_s:.0f} s vs GPU {gpu_ms_per_step:.2f} ms"),
-            "sample_cpu_s": round(q_time + g_time, 1)}
+            "sample": (f"every distinct (M, abits, layer) of the step: full activation "
+                       f"quantization ({q_time:.1f} s, 1 thread) and the GEMM on the first "
+                       f"{cols} output columns ({g_time:.1f} s, {threads} threads), GEMM time "
+                       f"scaled by N/{cols}; estimated oracle step {est_step_s:.0f} s vs GPU "
+                       f"{gpu_ms_per_step:.2f} ms"),
+            "sample_cpu_s": round(q_time + g_time, 1),
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
+            "single_thread_gops_toy_16x256x512": single(16, 256, 512, 7001),
+            "single_thread_gops_70b_down_m1": single(1, 8192, 28672, 7002)}
 
 
 if __name__ == "__main__":

@@ -53,6 +53,13 @@ SIGNATURES = {
     "flexq_linear_w6ax": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P,
                                          ctypes.c_size_t, _P, _P]),
 }
+# the on-device peak measurements of include/flexq_peaks.h
+PEAK_SIGNATURES = {
+    "flexq_peak_sink_bytes": (ctypes.c_size_t, []),
+    "flexq_peak_hbm_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
+    "flexq_peak_mfma_i8": (ctypes.c_int, [_I64, _I32, _P, _P, _P]),
+    "flexq_peak_mfma_i8_workgroups": (ctypes.c_int64, []),
+}
 
 _lib = None
 
@@ -72,7 +79,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
                                "(there is no CPU fallback)")
         h = ctypes.CDLL(LIB_PATH)  # after `import torch`, so the HIP runtime is shared
-        for name, (res, args) in SIGNATURES.items():
+        for name, (res, args) in {**SIGNATURES, **PEAK_SIGNATURES}.items():
             fn = getattr(h, name)
             fn.restype = res
             fn.argtypes = args
@@ -266,6 +273,35 @@ def gemm_w6ax_group_dots(q_a: torch.Tensor, w_packed: torch.Tensor, N: int,
                                             dots.data_ptr(), _stream(q_a)),
            "flexq_gemm_w6ax_group_dots")
     return dots
+
+
+def peak_hbm_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Enqueue flexq_peak_hbm_read over all of `buf` (a contiguous CUDA tensor whose
+    size is a multiple of 16 bytes); `sink`: uint8 CUDA tensor of peak_sink_bytes()."""
+    _tensor(sink, torch.uint8, "sink", min_bytes=peak_sink_bytes())
+    _on_gpu(buf=buf, sink=sink)
+    rc = lib().flexq_peak_hbm_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                   sink.data_ptr(), _stream(buf))
+    if rc != 0:
+        raise RuntimeError(f"flexq_peak_hbm_read returned {rc}")
+
+
+def peak_mfma_i8(iters: int, valu_per_mfma: int, sink: torch.Tensor,
+                 clock: torch.Tensor) -> int:
+    """Enqueue flexq_peak_mfma_i8; returns the integer ops the launch performs.
+    clock: int64 CUDA tensor of 2 (shader cycles, 100 MHz ticks of wave 0)."""
+    _tensor(sink, torch.uint8, "sink", min_bytes=peak_sink_bytes())
+    _tensor(clock, torch.int64, "clock", shape=(2,))
+    _on_gpu(sink=sink, clock=clock)
+    rc = lib().flexq_peak_mfma_i8(iters, valu_per_mfma, sink.data_ptr(), clock.data_ptr(),
+                                  _stream(sink))
+    if rc != 0:
+        raise RuntimeError(f"flexq_peak_mfma_i8 returned {rc}")
+    return 2 * 32768 * 4 * iters * 4 * int(lib().flexq_peak_mfma_i8_workgroups())
+
+
+def peak_sink_bytes() -> int:
+    return int(lib().flexq_peak_sink_bytes())
 
 
 def prefill_tile(M: int, N: int, K: int) -> int:

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libflexq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "pack_quant.hip", "gemm_decode.hip", "gemm_prefill.hip", "group_dots.hip"]
+SOURCES = ["api.hip", "pack_quant.hip", "gemm_decode.hip", "gemm_prefill.hip", "group_dots.hip",
+           "peaks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
