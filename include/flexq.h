@@ -190,6 +190,28 @@ flexq_status flexq_linear_w6ax(const uint16_t* x_fp16, const uint32_t* w_packed,
                                int32_t group_size, int32_t abits, void* workspace,
                                size_t workspace_bytes, uint16_t* y_fp16, void* stream);
 
+/* Bytes of device memory the library keeps on each GPU for
+   flexq_linear_w6ax_noalloc (64 MiB). */
+#define FLEXQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* flexq_linear_w6ax for callers that cannot allocate device memory or bring a
+   workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+   hipMalloc.  Same arguments and result (bit for bit) without the workspace: q_a and
+   s_a are staged in a file-scope device array of FLEXQ_NOALLOC_SCRATCH_BYTES bytes
+   inside the library, one per GPU, held until the process ends; its address is
+   looked up on the first call made with that device current.  The call allocates
+   nothing.  Shapes with flexq_linear_w6ax_workspace_bytes(M, K) above
+   FLEXQ_NOALLOC_SCRATCH_BYTES return FLEXQ_ERROR_UNSUPPORTED (e.g. K = 8192 allows
+   M <= 7943, K = 28672 allows M <= 2269).  All calls on one GPU share the array and
+   it keeps the last call's contents (nothing in it needs to start at zero): calls
+   ordered on one stream are safe, calls that may overlap in time on one GPU (other
+   streams, unordered host threads) race on it and must be serialized by the caller.
+   FLEXQ_ERROR_LAUNCH also when the runtime cannot resolve the array's address. */
+flexq_status flexq_linear_w6ax_noalloc(const uint16_t* x_fp16, const uint32_t* w_packed,
+                                       const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K,
+                                       int32_t group_size, int32_t abits, uint16_t* y_fp16,
+                                       void* stream);
+
 /* The int32 group dots d[m][n][g] (the integer products of the BTC section) computed
    with the same weight unpack and int8 MFMA as the GEMM; for verification.
      dots [M][N][K/128] int32, 4-byte aligned (output). */

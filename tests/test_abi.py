@@ -191,6 +191,33 @@ def test_linear_rejects_bad_arguments(flexq):
     assert call(N=0, wp=None, y=None, w=None, wb=0) == SUCCESS
 
 
+def test_linear_noalloc_rejects_bad_arguments(flexq):
+    """The allocation-free one-call layer checks its arguments like flexq_linear_w6ax
+    and refuses shapes whose staging exceeds its per-GPU array, all on the host."""
+    f = flexq.flexq_linear_w6ax_noalloc
+    big = 1 << 32   # fake addresses 4 GiB apart: large shapes do not overlap
+
+    def call(M=8, N=16, K=128, group=128, abits=6, x=A16, wp=3 * A16, sw=4 * A16, y=5 * A16):
+        return f(x, wp, sw, M, N, K, group, abits, y, None)
+
+    assert call(abits=7) == INVALID
+    assert call(x=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(M=-1) == INVALID
+    assert call(K=192) == UNSUPPORTED
+    assert call(N=40) == UNSUPPORTED
+    assert call(x=A16 + 8) == UNSUPPORTED
+    assert call(y=A16 + 64) == INVALID               # Y overlaps X
+    assert call(M=0, x=None, y=None) == SUCCESS
+    limit = 64 << 20
+    K = 28672
+    M_ok = 2269
+    assert flexq.flexq_linear_w6ax_workspace_bytes(M_ok, K) <= limit
+    assert flexq.flexq_linear_w6ax_workspace_bytes(M_ok + 1, K) > limit
+    assert call(M=M_ok + 1, K=K, x=big, wp=2 * big, sw=3 * big, y=4 * big) == UNSUPPORTED
+    assert call(M=8192, K=8192, x=big, wp=2 * big, sw=3 * big, y=4 * big) == UNSUPPORTED
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import w6a6_w6a8_integer_amd as fq

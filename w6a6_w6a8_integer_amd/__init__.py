@@ -52,6 +52,8 @@ SIGNATURES = {
     "flexq_linear_w6ax_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "flexq_linear_w6ax": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P,
                                          ctypes.c_size_t, _P, _P]),
+    "flexq_linear_w6ax_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P,
+                                                 _P]),
 }
 # the on-device peak measurements of include/flexq_peaks.h
 PEAK_SIGNATURES = {
@@ -60,6 +62,8 @@ PEAK_SIGNATURES = {
     "flexq_peak_mfma_i8": (ctypes.c_int, [_I64, _I32, _P, _P, _P]),
     "flexq_peak_mfma_i8_workgroups": (ctypes.c_int64, []),
 }
+# bytes of the library's per-GPU staging array behind flexq_linear_w6ax_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -253,6 +257,26 @@ def linear_w6ax(x: torch.Tensor, w_packed: torch.Tensor, s_w: torch.Tensor, N: i
     _check(lib().flexq_linear_w6ax(x.data_ptr(), w_packed.data_ptr(), s_w.data_ptr(), M, N, K,
                                    GROUP, abits, workspace.data_ptr(), workspace.numel(),
                                    y.data_ptr(), _stream(x)), "flexq_linear_w6ax")
+    return y
+
+
+def linear_w6ax_noalloc(x: torch.Tensor, w_packed: torch.Tensor, s_w: torch.Tensor, N: int,
+                        abits: int, y: torch.Tensor) -> torch.Tensor:
+    """flexq_linear_w6ax_noalloc: the one-call layer with its activation codes staged
+    in the library's own per-GPU device array, for callers that cannot allocate; the
+    caller passes the output.  Calls that may overlap in time on one GPU race on
+    that array (calls ordered on one stream are safe)."""
+    _matrix(x, torch.float16, "x")
+    M, K = x.shape
+    G = _groups(K, "linear_w6ax_noalloc")
+    N = _cols(N)
+    _packed(w_packed, N, K)
+    _tensor(s_w, torch.float16, "s_w", shape=(G, N))
+    _tensor(y, torch.float16, "y", shape=(M, N))
+    _on_gpu(x=x, w_packed=w_packed, s_w=s_w, y=y)
+    _check(lib().flexq_linear_w6ax_noalloc(x.data_ptr(), w_packed.data_ptr(), s_w.data_ptr(), M,
+                                           N, K, GROUP, abits, y.data_ptr(), _stream(x)),
+           "flexq_linear_w6ax_noalloc")
     return y
 
 

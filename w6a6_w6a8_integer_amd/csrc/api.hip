@@ -5,8 +5,16 @@
 // the caller's stream and returns FLEXQ_SUCCESS (or FLEXQ_ERROR_LAUNCH if the runtime
 // rejected a launch).  No memory is allocated; the only global state is the
 // per-device compute-unit count that the launch geometry uses (gemm_decode.hip).
+#include <atomic>
+
 #include "../../include/flexq.h"
 #include "kernels.h"
+
+// Staging memory of flexq_linear_w6ax_noalloc (activation codes, then their scales):
+// one copy of this array per GPU, held by the library until the process ends.  In
+// host code `scratch` is a host-side stand-in for the symbol, not a device address;
+// the address each GPU's copy has is looked up once per device (scratch_address).
+static __device__ __align__(256) unsigned char scratch[FLEXQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -79,6 +87,61 @@ flexq_status validate_gemm_operands(const int8_t* q_a, const float* s_a, const u
       overlap(o, range_of(s_w, (uint64_t)N * G * 2)))
     return FLEXQ_ERROR_INVALID_VALUE;
   return FLEXQ_SUCCESS;
+}
+
+// Argument checks of the one-call layer apart from its workspace.
+flexq_status validate_linear(const uint16_t* x_fp16, const uint32_t* w_packed,
+                             const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K,
+                             int32_t group_size, int32_t abits, const uint16_t* y_fp16) {
+  FLEXQ_TRY(check_m(M));
+  FLEXQ_TRY(check_n(N));
+  FLEXQ_TRY(check_k(K, group_size));
+  FLEXQ_TRY(check_scales(M, K));
+  FLEXQ_TRY(check_scales(N, K));
+  if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return FLEXQ_SUCCESS;
+  if (!x_fp16 || !w_packed || !s_w_fp16 || !y_fp16) return FLEXQ_ERROR_INVALID_VALUE;
+  if (!aligned(x_fp16, 16) || !aligned(w_packed, 16) || !aligned(s_w_fp16, 2) ||
+      !aligned(y_fp16, 4))
+    return FLEXQ_ERROR_UNSUPPORTED;
+  const uint64_t G = (uint64_t)(K / kGroup);
+  const Range ry = range_of(y_fp16, (uint64_t)M * N * 2);
+  if (overlap(ry, range_of(x_fp16, (uint64_t)M * K * 2)) ||
+      overlap(ry, range_of(w_packed, (uint64_t)N * K * 3 / 4)) ||
+      overlap(ry, range_of(s_w_fp16, (uint64_t)N * G * 2)))
+    return FLEXQ_ERROR_INVALID_VALUE;
+  return FLEXQ_SUCCESS;
+}
+
+// Device address of this GPU's copy of `scratch`: looked up with the current device
+// on the first call that needs it and kept per device (every GPU holds its own copy
+// at its own address).  nullptr if the runtime cannot resolve it.
+void* scratch_address() {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return nullptr;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// The one-call layer on validated arguments: quantize X into the workspace (q_a,
+// then s_a at the next 256-byte boundary), then the GEMM with the automatic choice.
+flexq_status run_linear(const uint16_t* x_fp16, const uint32_t* w_packed,
+                        const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K, int32_t abits,
+                        void* workspace, uint16_t* y_fp16, hipStream_t s) {
+  const int qmax = abits == 6 ? 31 : 127;
+  int8_t* q_a = static_cast<int8_t*>(workspace);
+  float* s_a = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        ((size_t)M * (size_t)K + 255) / 256 * 256);
+  FLEXQ_TRY(launched(flexq::launch_quant_act(x_fp16, M, K, qmax, q_a, s_a, s)));
+  if (flexq::auto_gemm_path(M, N) == FLEXQ_PATH_DECODE)
+    return launched(flexq::launch_gemm_decode(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
+  return launched(flexq::launch_gemm_prefill(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
 }
 
 }  // namespace
@@ -202,40 +265,35 @@ flexq_status flexq_linear_w6ax(const uint16_t* x_fp16, const uint32_t* w_packed,
                                const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K,
                                int32_t group_size, int32_t abits, void* workspace,
                                size_t workspace_bytes, uint16_t* y_fp16, void* stream) {
-  FLEXQ_TRY(check_m(M));
-  FLEXQ_TRY(check_n(N));
-  FLEXQ_TRY(check_k(K, group_size));
-  FLEXQ_TRY(check_scales(M, K));
-  FLEXQ_TRY(check_scales(N, K));
-  if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
+  FLEXQ_TRY(validate_linear(x_fp16, w_packed, s_w_fp16, M, N, K, group_size, abits, y_fp16));
   if (M == 0 || N == 0) return FLEXQ_SUCCESS;
-  if (!x_fp16 || !w_packed || !s_w_fp16 || !y_fp16) return FLEXQ_ERROR_INVALID_VALUE;
-  if (!aligned(x_fp16, 16) || !aligned(w_packed, 16) || !aligned(s_w_fp16, 2) ||
-      !aligned(y_fp16, 4))
-    return FLEXQ_ERROR_UNSUPPORTED;
   const size_t ws = flexq_linear_w6ax_workspace_bytes(M, K);
   if (!workspace || workspace_bytes < ws) return FLEXQ_ERROR_INVALID_VALUE;
   if (!aligned(workspace, 16)) return FLEXQ_ERROR_UNSUPPORTED;
   const uint64_t G = (uint64_t)(K / kGroup);
-  const Range rx = range_of(x_fp16, (uint64_t)M * K * 2);
-  const Range rw = range_of(w_packed, (uint64_t)N * K * 3 / 4);
-  const Range rs = range_of(s_w_fp16, (uint64_t)N * G * 2);
-  const Range ry = range_of(y_fp16, (uint64_t)M * N * 2);
   const Range rk = range_of(workspace, ws);
-  if (overlap(ry, rx) || overlap(ry, rw) || overlap(ry, rs))
+  if (overlap(rk, range_of(x_fp16, (uint64_t)M * K * 2)) ||
+      overlap(rk, range_of(w_packed, (uint64_t)N * K * 3 / 4)) ||
+      overlap(rk, range_of(s_w_fp16, (uint64_t)N * G * 2)) ||
+      overlap(rk, range_of(y_fp16, (uint64_t)M * N * 2)))
     return FLEXQ_ERROR_INVALID_VALUE;
-  if (overlap(rk, rx) || overlap(rk, rw) || overlap(rk, rs) || overlap(rk, ry))
-    return FLEXQ_ERROR_INVALID_VALUE;
-  const int qmax = abits == 6 ? 31 : 127;
-  hipStream_t s = (hipStream_t)stream;
-  int8_t* q_a = static_cast<int8_t*>(workspace);
-  float* s_a = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        ((size_t)M * (size_t)K + 255) / 256 * 256);
-  FLEXQ_TRY(launched(flexq::launch_quant_act(x_fp16, M, K, qmax, q_a, s_a, s)));
-  const int path = flexq::auto_gemm_path(M, N);
-  if (path == FLEXQ_PATH_DECODE)
-    return launched(flexq::launch_gemm_decode(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
-  return launched(flexq::launch_gemm_prefill(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
+  return run_linear(x_fp16, w_packed, s_w_fp16, M, N, K, abits, workspace, y_fp16,
+                    (hipStream_t)stream);
+}
+
+flexq_status flexq_linear_w6ax_noalloc(const uint16_t* x_fp16, const uint32_t* w_packed,
+                                       const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K,
+                                       int32_t group_size, int32_t abits, uint16_t* y_fp16,
+                                       void* stream) {
+  FLEXQ_TRY(validate_linear(x_fp16, w_packed, s_w_fp16, M, N, K, group_size, abits, y_fp16));
+  if (M == 0 || N == 0) return FLEXQ_SUCCESS;
+  if (flexq_linear_w6ax_workspace_bytes(M, K) > (size_t)FLEXQ_NOALLOC_SCRATCH_BYTES)
+    return FLEXQ_ERROR_UNSUPPORTED;
+  void* ws = scratch_address();
+  if (ws == nullptr) return FLEXQ_ERROR_LAUNCH;
+  // the quantizer writes every byte of q_a and s_a that the GEMM reads, so nothing
+  // left in the array by an earlier call is ever used
+  return run_linear(x_fp16, w_packed, s_w_fp16, M, N, K, abits, ws, y_fp16, (hipStream_t)stream);
 }
 
 flexq_status flexq_gemm_w6ax_group_dots(const int8_t* q_a, const uint32_t* w_packed, int64_t M,
