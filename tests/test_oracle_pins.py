@@ -543,3 +543,34 @@ def test_end_to_end_worked_vector(abits):
     # the same through the packed weights
     wp, sw2 = oracle.pack_w6(w)
     assert int(oracle.gemm_packed(qa, sa, wp, sw2, 16)[0, 0].view(np.uint16)) == ref["y"]
+
+
+# ---------------------------------------------------------------------------
+# the oracle's C code under the address and undefined-behaviour sanitizers
+# ---------------------------------------------------------------------------
+
+def test_oracle_runs_clean_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """tests/oracle_sanitize_driver.c runs every oracle function (ordinary, zero,
+    extreme and subnormal groups; 1 and several threads; argument errors) in a gcc
+    build of oracle/flexq_oracle.c with -fsanitize=address,undefined; any memory or
+    undefined-behaviour error aborts the run."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    here = os.path.dirname(os.path.abspath(__file__))
+    exe = str(tmp_path / "oracle_sanitized")
+    subprocess.check_call([gcc, "-std=c11", "-O1", "-g", "-pthread", "-ffp-contract=off",
+                           "-fno-fast-math", "-fsanitize=address,undefined",
+                           "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+                           os.path.join(here, "oracle_sanitize_driver.c"),
+                           os.path.join(os.path.dirname(here), "oracle", "flexq_oracle.c"),
+                           "-o", exe, "-lm"])
+    # (verify_asan_link_order=0: the environment may preload a library ahead of ASan's)
+    env = dict(os.environ,
+               ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:verify_asan_link_order=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "clean" in r.stdout
