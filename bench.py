@@ -9,10 +9,15 @@ resident in HBM.  Weights are packed once, before timing (offline step).
 
 Prints one JSON line: value = whole-step GEMM+quant throughput in TOPS (2*M*N*K
 integer ops per GEMM, M unpadded), per-shape TOPS / GB/s / roofline fractions,
-the roofline of the dominant kernel and the CPU oracle timed on a bounded sample.
-The step is first run launch by launch with events around every kernel (per-kernel
-figures), then captured once as a HIP graph whose replays give ms_per_step and
-value (the same kernels without host launch gaps; --eager keeps the eager time).
+the roofline of the dominant kernel, on-device peak measurements and the CPU
+oracle timed on a bounded sample.  The step is captured once as a HIP graph whose
+replays give ms_per_step and value (--eager: the launch-by-launch step instead).
+Per-kernel figures come from runs of --reps back-to-back launches of each shape
+between HIP events (the GEMM rotating over weight copies so none is served from
+the Infinity Cache), medians and p10 / p90 over --steps runs.
+--summarize-trace DB turns a rocprofv3 kernel trace of such a run into the
+markdown tables kept under profiles/, with the same figures recomputed from the
+kernel durations.
 """
 from __future__ import annotations
 
@@ -48,6 +53,7 @@ ABITS = (6, 8)
 
 
 TILE_NAMES = {3: "256x128", 4: "128x128", 5: "128x64"}
+REPS_IN_RUN = 20   # back-to-back launches per timed run of one shape
 
 
 def gemm_bytes(M, N, K):
@@ -80,6 +86,13 @@ def parse():
                         "70b_tp8: one GPU's share of them under 8-way tensor parallelism; "
                         "70b_stack: all 80 decoder layers resident (52 GB packed), a decode "
                         "pass at M = 32 and a prefill pass at M = 2048, A8 on 8 seeded layers")
+    p.add_argument("--reps", type=int, default=REPS_IN_RUN,
+                   help="back-to-back launches per timed run of one shape (fewer for "
+                        "counter-collection runs, where every launch is profiled)")
+    p.add_argument("--summarize-trace", metavar="DB", default=None,
+                   help="print a markdown summary of a rocprofv3 --kernel-trace database of a "
+                        "bench run (per-kernel times, GEMM launches by grid, the prefill "
+                        "kernel's int8 fraction recomputed from the trace) and exit")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="first run one device-to-device copy of this many MiB (the known-size "
                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -117,8 +130,96 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def summarize_trace(db, layers, m_list, reps):
+    """Markdown summary of a rocprofv3 kernel-trace database (the `kernels` view of
+    its SQLite output) of a bench run on `layers` at token counts `m_list`."""
+    import sqlite3
+    import w6a6_w6a8_integer_amd as fq
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, duration, grid_x, workgroup_x from kernels").fetchall()
+    print("| kernel | calls | total (us) | average (us) | share % |\n|---|---|---|---|---|")
+    tot = sum(r[1] for r in rows)
+    agg = {}
+    for name, dur, gx, wx in rows:
+        a = agg.setdefault(name, [0, 0.0])
+        a[0] += 1
+        a[1] += dur
+    for name, (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        print(f"| `{name[:90]}` | {n} | {t / 1e3:.1f} | {t / n / 1e3:.2f} | {100 * t / tot:.2f} |")
+    # GEMM launches by (kernel, grid): prefill launches matched to their shapes by tile
+    # and grid (the tail split's two kernels per call both counted)
+    grids = {}
+    for name, dur, gx, wx in rows:
+        if "gemm_" in name:
+            g = grids.setdefault((name, gx // max(wx, 1)), [])
+            g.append(dur)
+    print("\n| kernel | workgroups | calls | avg (us) | min (us) | max (us) |\n|---|---|---|---|---|---|")
+    for (name, wg), d in sorted(grids.items()):
+        short = name.split("(")[0].replace("void ", "")
+        print(f"| `{short}` | {wg} | {len(d)} | {sum(d) / len(d) / 1e3:.2f} | {min(d) / 1e3:.2f} "
+              f"| {max(d) / 1e3:.2f} |")
+    # The per-kernel runs of the bench, recognized in dispatch order: a busy kernel,
+    # REPS_IN_RUN quantizer launches, then the GEMM launches of one (M, abits, layer)
+    # (two kernels per call where the prefill tail split applies); runs come in the
+    # bench's shape order, `steps` times over.
+    ordered = con.execute("select name, duration from kernels order by start").fetchall()
+    keys = sorted({(M, ab, n) for M in m_list for ab in ABITS for n in layers},
+                  key=lambda k: (-k[0], k[1], list(layers).index(k[2])))
+    runs, i = [], 0
+    while i < len(ordered):
+        if "peak_mfma_kernel" in ordered[i][0]:
+            j = i + 1
+            nq = 0
+            while j < len(ordered) and "quant_act_kernel" in ordered[j][0]:
+                j += 1
+                nq += 1
+            g = []
+            while j < len(ordered) and "gemm_" in ordered[j][0]:
+                g.append(ordered[j][1])
+                j += 1
+            if nq == reps and g:
+                runs.append(g)
+            i = j
+        else:
+            i += 1
+    if not runs or len(runs) % len(keys):
+        print(f"\n{len(runs)} per-kernel runs found; expected a multiple of {len(keys)}")
+        return
+    per_key = {k: [] for k in keys}
+    for r, g in enumerate(runs):
+        per_key[keys[r % len(keys)]].append(sum(g) / reps)   # ns per call
+    pre_ops = pre_ns = dec_b = dec_ns = 0.0
+    print("\n| layer | M | abits | kernel | trace us per call (median of runs) |\n|---|---|---|---|---|")
+    for k in sorted(keys, key=lambda k: (k[0], k[1], list(layers).index(k[2]))):
+        M, ab, name = k
+        N, K = layers[name]
+        t = statistics.median(per_key[k])
+        dec = fq.auto_path(M, N, K) == fq.PATH_DECODE
+        print(f"| {name} | {M} | {ab} | {'decode' if dec else 'prefill'} | {t / 1e3:.2f} |")
+        if dec and M <= 16:
+            dec_b += gemm_bytes(M, N, K)
+            dec_ns += t
+        if not dec:
+            pre_ops += 2.0 * M * N * K
+            pre_ns += t
+    if pre_ns:
+        tops = pre_ops / (pre_ns * 1e-9) / 1e12
+        print(f"\nFrom the trace: prefill {tops:.1f} TOP/s = {tops / INT8_PEAK_TOPS:.4f} of "
+              f"{INT8_PEAK_TOPS:.0f} (the bench's roofline.frac), "
+              f"M >= 1024 only: see the rows above; decode at M <= 16: "
+              f"{dec_b / (dec_ns * 1e-9) / 1e9:.1f} GB/s = "
+              f"{dec_b / (dec_ns * 1e-9) / 1e9 / HBM_PEAK_GBS:.4f} of {HBM_PEAK_GBS:.0f} "
+              f"(the bench's hbm_frac_m_le_16); {len(runs)} runs of {reps} calls")
+
+
 def main():
+    global LAYERS
     args = parse()
+    if args.summarize_trace:
+        m_list = tuple(int(v) for v in args.m.split(",")) if args.m else M_LIST
+        summarize_trace(args.summarize_trace, LAYERS_TP8 if args.layers == "70b_tp8" else LAYERS,
+                        m_list, args.reps)
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(sharding over GPUs is designed, not built)", file=sys.stderr)
@@ -127,7 +228,6 @@ def main():
     import torch
     import w6a6_w6a8_integer_amd as fq
 
-    global LAYERS
     if args.layers == "70b_tp8":
         LAYERS = LAYERS_TP8
     fq.lib()
@@ -161,12 +261,14 @@ def main():
     ncopies = max(2, -(-(1 << 30) // int(set_bytes)))
     if stack:
         ncopies = STACK_LAYERS  # one resident copy per decoder layer (same synthetic values)
+    # The per-kernel runs launch one layer back to back: each layer gets enough copies
+    # that a copy returns only after at least 1.2 GB of its other copies.
     for li, (name, (N, K)) in enumerate(LAYERS.items()):
         w = synth.weights(synth.derive_seed(args.seed, "70b", name, "w"), N, K, nthreads=nthreads)
         wd = torch.from_numpy(w).to(dev)
         del w
         copies = []
-        for c in range(ncopies):
+        for c in range(max(ncopies, -(-int(1.2e9) // int(gemm_bytes(1, N, K))))):
             copies.append(fq.pack_w6(wd))
         del wd
         packed[name] = copies
@@ -220,29 +322,55 @@ def main():
         step(False)
     torch.cuda.synchronize()
 
-    quant_ms = {k: [] for k in keys}
-    gemm_ms = {k: [] for k in keys}
+    # The step launch by launch, with events around every kernel (the in-step times).
+    step_gemm_ms = {k: [] for k in keys}
     step_ms = []
-    # Per-kernel times come from events around every launch of the eager steps.  A
-    # busy kernel (about 10 ms of MFMA work) holds the GPU before each such step, so
-    # the host has queued the whole step -- every launch and event -- before the GPU
-    # reaches it: the events then time the kernels back to back, not the host's
-    # launch path.
-    sink = torch.empty(fq.peak_sink_bytes(), dtype=torch.uint8, device=dev)
-    clock = torch.zeros(2, dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     wall0 = time.time()
     for s in range(args.steps):
-        fq.peak_mfma_i8(80000, 0, sink, clock)
         step(True)
         torch.cuda.synchronize()  # read this step's events
         for i, e in enumerate(plan):
-            quant_ms[e[:3]].append(ev[i][0].elapsed_time(ev[i][1]))
-            gemm_ms[e[:3]].append(ev[i][1].elapsed_time(ev[i][2]))
+            step_gemm_ms[e[:3]].append(ev[i][1].elapsed_time(ev[i][2]))
         step_ms.append(ev[0][0].elapsed_time(ev[-1][2]))
     wall = time.time() - wall0
     total_ms = sum(step_ms)
     ms_per_step_eager = statistics.median(step_ms)
+
+    # Per-kernel times: every (M, abits, layer) GEMM, and its activation quantization,
+    # launched REPS times back to back (the GEMM on rotating weight copies, at least
+    # 1.2 GB apart), between two events; `steps` such runs give the median and
+    # p10 / p90 of the time per launch.  A busy kernel (about 10 ms of MFMA work)
+    # holds the GPU before each run, so the host has queued the whole run before the
+    # GPU reaches it.  Events around single launches would add the inter-kernel gap
+    # and the event packets (a few us) to every launch, a fifth of the small layers'
+    # time.
+    REPS = args.reps
+    quant_ms = {k: [] for k in keys}
+    gemm_ms = {k: [] for k in keys}
+    sink = torch.empty(fq.peak_sink_bytes(), dtype=torch.uint8, device=dev)
+    clock = torch.zeros(2, dtype=torch.int64, device=dev)
+    r0, r1, r2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    wall1 = time.time()
+    for s in range(args.steps):
+        for k in keys:
+            M, ab, name = k
+            N, K = LAYERS[name]
+            _, xd, qa, sa, y = bufs[(M, name)]
+            cps = packed[name]
+            fq.peak_mfma_i8(80000, 0, sink, clock)
+            r0.record()
+            for j in range(REPS):
+                fq.quant_act(xd, ab, q_a=qa, s_a=sa)
+            r1.record()
+            for j in range(REPS):
+                wp, sw = cps[(s * REPS + j) % len(cps)]
+                fq.gemm_w6ax(qa, sa, wp, sw, N, ab, y=y)
+            r2.record()
+            torch.cuda.synchronize()
+            quant_ms[k].append(r0.elapsed_time(r1) / REPS)
+            gemm_ms[k].append(r1.elapsed_time(r2) / REPS)
+    wall += time.time() - wall1
 
     # The same step captured once as a HIP graph and replayed back to back: the kernels
     # and their arguments are the eager step's (the same weight copies); ms_per_step
@@ -277,7 +405,7 @@ def main():
     kernel_of = {k: ("decode" if fq.auto_path(k[0], *LAYERS[k[2]]) == fq.PATH_DECODE
                      else "prefill") for k in keys}
     tot_ops = sum(2.0 * e[0] * LAYERS[e[2]][0] * LAYERS[e[2]][1] for e in plan)
-    per_step = {k: len(gemm_ms[k]) // len(step_ms) for k in keys}
+    per_step = {k: len(step_gemm_ms[k]) // len(step_ms) for k in keys}
 
     def pct(v, q):
         v = sorted(v)
@@ -297,7 +425,9 @@ def main():
         row = [name, M, ab, "decode" if dec else TILE_NAMES[fq.prefill_tile(M, N, K)]
                + ("+128x64" if fq.prefill_main_cols(M, N, K) < N else ""),
                round(g * 1e3, 2), round(pct(gemm_ms[k], 0.1) * 1e3, 2),
-               round(pct(gemm_ms[k], 0.9) * 1e3, 2), round(statistics.median(quant_ms[k]) * 1e3, 2),
+               round(pct(gemm_ms[k], 0.9) * 1e3, 2),
+               round(statistics.median(step_gemm_ms[k]) * 1e3, 2),
+               round(statistics.median(quant_ms[k]) * 1e3, 2),
                round(ops / (g * 1e-3) / 1e12, 1), round(by / (g * 1e-3) / 1e9, 1),
                round(by / (g * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
                round(ops / (g * 1e-3) / 1e12 / INT8_PEAK_TOPS, 3)]
@@ -308,22 +438,23 @@ def main():
                        else round(ops / (g * 1e-3) / 1e12 / peaks["mfma_i8_tops"], 3))
         shapes.append(row)
     shape_cols = ["layer", "M", "abits", "kernel", "gemm_us_median", "gemm_us_p10",
-                  "gemm_us_p90", "quant_us_median", "tops", "gbs", "frac_hbm_8tbs",
+                  "gemm_us_p90", "gemm_us_in_step", "quant_us_median", "tops", "gbs", "frac_hbm_8tbs",
                   "frac_int8_5pops"] + (["frac_measured_peak"] if peaks else [])
 
     def over(sel, kern):
-        """Summed algorithmic bytes / ops over summed event times of the selected GEMMs."""
+        """Algorithmic bytes / ops over the time of the selected GEMMs, each counted as
+        often as a step runs it, at its median time per launch."""
         ks = [k for k in keys if sel(k[0]) and kernel_of[k] == kern]
-        ms = sum(sum(gemm_ms[k]) for k in ks)
+        ms = sum(per_step[k] * statistics.median(gemm_ms[k]) for k in ks)
         if not ms:
             return None
-        byt = sum(gemm_bytes(k[0], *LAYERS[k[2]]) * len(gemm_ms[k]) for k in ks)
-        ops = sum(2.0 * k[0] * LAYERS[k[2]][0] * LAYERS[k[2]][1] * len(gemm_ms[k]) for k in ks)
+        byt = sum(per_step[k] * gemm_bytes(k[0], *LAYERS[k[2]]) for k in ks)
+        ops = sum(per_step[k] * 2.0 * k[0] * LAYERS[k[2]][0] * LAYERS[k[2]][1] for k in ks)
         r = {"gbs": byt / (ms * 1e-3) / 1e9, "tops": ops / (ms * 1e-3) / 1e12, "ms": ms}
         if peaks:
             # time each launch would take at the plain-read rate of its layer's size
-            ideal = sum(gemm_bytes(k[0], *LAYERS[k[2]]) / (peaks["hbm_read_gbs"][k[2]] * 1e9)
-                        * len(gemm_ms[k]) for k in ks)
+            ideal = sum(per_step[k] * gemm_bytes(k[0], *LAYERS[k[2]])
+                        / (peaks["hbm_read_gbs"][k[2]] * 1e9) for k in ks)
             r["hbm_frac_measured"] = ideal / (ms * 1e-3)
         return r
 
@@ -354,7 +485,8 @@ def main():
                     # counters were taken on the default workload's launches only
                     "traffic": (recorded_traffic() if args.layers == "70b" and not args.m
                                 else None),
-                    "timing": "HIP events around each launch on its stream, all steps",
+                    "timing": (f"median over runs of {args.reps} back-to-back launches between HIP "
+                               "events on the launch stream"),
                     "launches_per_step": pre_launches, "kernel_launches_per_step": pre_kernels,
                     "ops_per_launch": round(sum(2.0 * k[0] * LAYERS[k[2]][0] * LAYERS[k[2]][1]
                                                 * per_step[k] for k in keys
@@ -366,7 +498,8 @@ def main():
         roofline = {"kernel": "gemm_decode_kernel", "bound": "hbm",
                     "achieved": round(dec_all["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(dec_all["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
-                    "timing": "HIP events around each launch on its stream, all steps"}
+                    "timing": (f"median over runs of {args.reps} back-to-back launches between "
+                               "HIP events on the launch stream")}
     # the two target figures also as scalars of the roofline record
     roofline["hbm_frac_m_le_16"] = targets["hbm_frac_m_le_16"]
     roofline["int8_frac_m_ge_1024"] = targets["int8_frac_m_ge_1024"]

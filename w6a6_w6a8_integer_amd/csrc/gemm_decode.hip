@@ -353,7 +353,7 @@ static hipError_t launch_decode_c(const int8_t* qa, const float* sa, const uint3
 template <int MT, int T, int S, int P, int CMAX>
 static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint32_t* wp,
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
-                                  uint16_t* y, hipStream_t stream) {
+                                  uint16_t* y, hipStream_t stream, bool chunk_few_rows = false) {
   const int64_t ntiles16 = N / 16;
   const int64_t ntiles = (ntiles16 + T - 1) / T;
   const int64_t items = ntiles * ((M + 63) / 64);
@@ -362,9 +362,10 @@ static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint3
   const int64_t grid0 = std::min<int64_t>(items, device_cu_count());
   const int64_t per_wg = (items + grid0 - 1) / grid0;
   const int64_t grid = (items + per_wg - 1) / per_wg;
-  // chunk: the workgroup's items share each round's activation fragments (not worth
-  // the empty steps of a partial chunk when there are only a few token rows)
-  if (M <= 4)
+  // chunk: the workgroup's items share each round's activation fragments (with only a
+  // few token rows not worth the empty steps of a partial chunk, except where the
+  // caller found it pays)
+  if (M <= 4 && !chunk_few_rows)
     return launch_decode_c<MT, T, S, P, 1>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items,
                                            per_wg, grid, stream);
   if (CMAX >= 8 && per_wg >= 5)
@@ -385,13 +386,22 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
                               hipStream_t stream) {
   // rows per pass: 16 * MT; more passes over W only when M > 64
   const int64_t rows = M > 64 ? 64 : M;
+  const int64_t cu = device_cu_count();
   if (rows <= 16) {
     // Narrow, short layers (up to 3 single-tile items per CU, K <= 16384) run single
     // tiles: the workgroups' shares of the weights come out more even (10 % faster on
     // the 70B qkv and o shapes); elsewhere pairing tiles halves the activation
-    // fragment loads per weight byte and wins.
-    if (N / 16 <= 3 * (int64_t)device_cu_count() && K <= 16384)
+    // fragment loads per weight byte and wins.  Up to 4 rows, chunks of 2 items share
+    // the activation fragments, and layers with more than 2 single tiles per CU pair
+    // their tiles (back-to-back launches, 70B at M = 1: qkv 16.3 -> 14.8 us with
+    // paired tiles, o 12.3 -> 11.3 us with chunks of single tiles).
+    if (N / 16 <= 3 * cu && K <= 16384) {
+      if (rows <= 4 && N / 16 > 2 * cu)
+        return launch_decode_t<1, 2, 16, 2, 2>(qa, sa, wp, sw, M, N, K, y, stream, true);
+      if (rows <= 4)
+        return launch_decode_t<1, 1, 16, 2, 2>(qa, sa, wp, sw, M, N, K, y, stream, true);
       return launch_decode_t<1, 1, 16, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
+    }
     // Paired tiles: 16 waves for up to 4 rows; from 5 rows 8 waves with the
     // column-segment fold (70B down at M = 16: 39 -> 36 us; 16 waves stay faster
     // at M = 1, where the fold is tiny and more waves keep more loads in flight).
@@ -403,7 +413,7 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
     // Paired tiles take 8 waves: the register budget then allows chunks of 8 items
     // (activation fragments shared 8 ways; 16 waves fit only 2) and the column-
     // segment fold (70B gate_up at M = 24 / 32: 80 -> 67 / 90 -> 73 us).
-    if (N / 16 <= 3 * (int64_t)device_cu_count() && K <= 16384)
+    if (N / 16 <= 3 * cu && K <= 16384)
       return launch_decode_t<2, 1, 16, 2, 4>(qa, sa, wp, sw, M, N, K, y, stream);
     return launch_decode_t<2, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
   }
