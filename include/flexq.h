@@ -84,7 +84,9 @@ typedef enum {
      tuning; every tile accepts every shape and gives the same bits */
   FLEXQ_PATH_PREFILL_256X128 = 3,
   FLEXQ_PATH_PREFILL_128X128 = 4,
-  FLEXQ_PATH_PREFILL_128X64 = 5
+  FLEXQ_PATH_PREFILL_128X64 = 5,
+  /* 256 x 128 tiles computed by 4 MFMA waves while 4 loader waves stage the operands */
+  FLEXQ_PATH_PREFILL_256X128_WS = 6
 } flexq_path;
 
 #define FLEXQ_ABI_VERSION 1

@@ -373,7 +373,7 @@ def test_prefill_tail_split_rule(flexq):
 
 def test_gemm_path_values(flexq):
     f = flexq.flexq_gemm_w6ax_path
-    for bad in (-1, 6, 7):
+    for bad in (-1, 7, 8):
         assert f(A16, 2 * A16, 3 * A16, 4 * A16, 4, 16, 128, 128, 6, bad, 5 * A16, None) == INVALID
-    for p in range(6):  # every valid path with M = 0: a no-op
+    for p in range(7):  # every valid path with M = 0: a no-op
         assert f(None, None, 3 * A16, 4 * A16, 0, 16, 128, 128, 6, p, None, None) == SUCCESS

@@ -12,7 +12,7 @@ LIB = os.path.join(PKG, "libflexq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.hip", "pack_quant.hip", "gemm_decode.hip", "gemm_prefill.hip", "group_dots.hip",
-           "peaks.hip"]
+           "peaks.hip", "gemm_prefill_ws.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -135,6 +135,9 @@ flexq_status run_linear(const uint16_t* x_fp16, const uint32_t* w_packed,
                         const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K, int32_t abits,
                         void* workspace, uint16_t* y_fp16, hipStream_t s) {
   const int qmax = abits == 6 ? 31 : 127;
+  if (flexq::fused_quant_eligible(M, N, K))   // one kernel; the workspace is not touched
+    return launched(flexq::launch_linear_decode_fused(x_fp16, M, K, qmax, w_packed, s_w_fp16, N,
+                                                      y_fp16, s));
   int8_t* q_a = static_cast<int8_t*>(workspace);
   float* s_a = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         ((size_t)M * (size_t)K + 255) / 256 * 256);
@@ -212,7 +215,8 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a, const uin
   FLEXQ_TRY(check_scales(M, K));
   FLEXQ_TRY(check_scales(N, K));
   if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
-  if (path < FLEXQ_PATH_AUTO || path > FLEXQ_PATH_PREFILL_128X64) return FLEXQ_ERROR_INVALID_VALUE;
+  if (path < FLEXQ_PATH_AUTO || path > FLEXQ_PATH_PREFILL_256X128_WS)
+    return FLEXQ_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return FLEXQ_SUCCESS;
   FLEXQ_TRY(validate_gemm_operands(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16,
                                    (uint64_t)M * N * 2));
@@ -220,6 +224,9 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a, const uin
   hipStream_t s = (hipStream_t)stream;
   if (path == FLEXQ_PATH_DECODE)
     return launched(flexq::launch_gemm_decode(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
+  if (path == FLEXQ_PATH_PREFILL_256X128_WS)
+    return launched(
+        flexq::launch_gemm_prefill_ws(q_a, s_a, w_packed, s_w_fp16, M, 0, N, K, N, y_fp16, s));
   const int tile = path == FLEXQ_PATH_PREFILL_256X128   ? flexq::kTile256x128
                    : path == FLEXQ_PATH_PREFILL_128X128 ? flexq::kTile128x128
                    : path == FLEXQ_PATH_PREFILL_128X64  ? flexq::kTile128x64

@@ -78,11 +78,16 @@ struct Cursor {
 
 }  // namespace
 
-template <int MT, int T, int S, int P, int C>
+// FQ: the activation quantization fused in front (one pass of up to 16 rows): the
+// workgroup quantizes fp16 X (x, qmax) once into LDS -- the same per-group rule and
+// helper as flexq_quant_act, so codes and scales are bit-identical -- and the
+// activation fragments and scales are read from there instead of q_a / s_a.
+template <int MT, int T, int S, int P, int C, bool FQ>
 __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint32_t* __restrict__ wp,
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ y, int ntiles16,
-    int ntiles, int items, int per_wg) {
+    int ntiles, int items, int per_wg, const uint16_t* __restrict__ x, int qmax) {
+  static_assert(!FQ || MT == 1, "the fused quantizer covers one pass of up to 16 rows");
   static_assert(P % 2 == 0, "slot parity must be static");
   constexpr int U = C > P ? C : P;  // steps per loop iteration: ring slot and item static
   static_assert(U % P == 0 && U % C == 0, "step unroll");
@@ -111,6 +116,11 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
   __shared__ __attribute__((aligned(16))) int32_t lds_d[2][S][PARK];
   __shared__ __attribute__((aligned(16))) float lds_sa[2][S][ROWS];
   __shared__ float lds_sw[2][S][COLS];
+  // FQ: the quantized activations, [rows][K] codes then [G][rows] scales
+  extern __shared__ __attribute__((aligned(16))) int8_t lds_x[];
+  const int fq_rows = FQ ? min(ROWS, M) : 0;
+  const int8_t* lq = lds_x;
+  const float* lsc = reinterpret_cast<const float*>(lds_x + (fq_rows * K + 15) / 16 * 16);
 
   const uint32_t a_lane_off = (uint32_t)(lane & 15) * (uint32_t)K + (uint32_t)(lane >> 4) * 16u;
 
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
       b.w[t][1] =
           __builtin_amdgcn_raw_buffer_load_b96(rw, (g * 128u + 64u + lane) * 12u, 0, kNonTemporal);
     }
-    if constexpr (decltype(first_slot)::value) {
+    if constexpr (decltype(first_slot)::value && !FQ) {
 #pragma unroll
       for (int ms = 0; ms < MT; ++ms) {
 #pragma unroll
@@ -150,8 +160,9 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
     }
     // (every offset goes in the VGPR operand: the range check that zeroes reads
     // past the buffer does not cover the scalar offset)
-    b.sa = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rsa, ((uint32_t)lane + g * (uint32_t)M) * 4u, 0, 0));
+    if constexpr (!FQ)
+      b.sa = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rsa, ((uint32_t)lane + g * (uint32_t)M) * 4u, 0, 0));
     b.sw = __builtin_amdgcn_raw_buffer_load_b16(
         rsw, ((uint32_t)(lane % COLS) + g * (uint32_t)N) * 2u, 0, 0);
   };
@@ -165,6 +176,28 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
     load(ring[p], cl, std::integral_constant<bool, p % C == 0>{});
     cl.next(C, R, item_end, ntiles);
   }, std::make_integer_sequence<int, P>{});
+
+  if constexpr (FQ) {
+    // quantize the pass's rows into LDS while the weight loads above are in flight:
+    // unit u = 8 consecutive values; the 16 units of a 128-deep group sit in the 16
+    // lanes of one DPP row (rows * K / 8 and the loop step are multiples of 16, so a
+    // DPP row is wholly inside or outside the range)
+    int8_t* wq = lds_x;
+    float* ws = reinterpret_cast<float*>(lds_x + (fq_rows * K + 15) / 16 * 16);
+    const int upr = K >> 3, units = fq_rows * upr;
+    for (int u0 = 0; u0 < units; u0 += THREADS) {
+      const int u = u0 + (int)threadIdx.x;
+      if (u < units) {
+        const int row = u / upr, k0 = (u - row * upr) * 8;
+        const u32x4 h = *reinterpret_cast<const u32x4*>(x + (size_t)row * K + k0);
+        float s;
+        const u32x2 codes = quant8_row16(h, qmax, s);
+        *reinterpret_cast<u32x2*>(wq + row * K + k0) = codes;
+        if ((threadIdx.x & 15) == 0) ws[(k0 >> 7) * fq_rows + row] = s;
+      }
+    }
+    __syncthreads();
+  }
 
   float acc[C][OPT];
 #pragma unroll
@@ -181,11 +214,22 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
       constexpr int slot = p & 1;
       constexpr int ci = p % C;  // item slot of this step
       Bundle<MT, T>& b = ring[p % P];
+      // FQ: this step's group in the LDS copy (clamped: rounds past the last group
+      // are never folded), and a row that exists (rows past M are never stored)
+      const int fq_g = FQ ? min(cp.r * S + wave, G - 1) : 0;
       if constexpr (ci == 0) {
+        if constexpr (FQ) {
+          const int row = min(lane & 15, fq_rows - 1);
 #pragma unroll
-        for (int ms = 0; ms < MT; ++ms) {
-          a_cur[ms][0] = b.a[ms][0];
-          a_cur[ms][1] = b.a[ms][1];
+          for (int j = 0; j < 2; ++j)
+            a_cur[0][j] = *reinterpret_cast<const i32x4*>(lq + row * K + fq_g * 128 + j * 64 +
+                                                          (lane >> 4) * 16);
+        } else {
+#pragma unroll
+          for (int ms = 0; ms < MT; ++ms) {
+            a_cur[ms][0] = b.a[ms][0];
+            a_cur[ms][1] = b.a[ms][1];
+          }
         }
       }
       // exact integer group products (4*d, see w6_device.h)
@@ -217,7 +261,11 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
                   d[t][ms][i];
           }
         }
-      if (lane < ROWS) lds_sa[slot][wave][lane] = b.sa;
+      if constexpr (FQ) {
+        if (lane < ROWS) lds_sa[slot][wave][lane] = lsc[fq_g * fq_rows + min(lane, fq_rows - 1)];
+      } else {
+        if (lane < ROWS) lds_sa[slot][wave][lane] = b.sa;
+      }
       if (lane < COLS) lds_sw[slot][wave][lane] = 0.25f * half_bits_to_float((uint16_t)b.sw);
       // the step P ahead lands in this ring slot; it is the chunk's first item slot
       // exactly when this one is (P is a multiple of C, or C of P)
@@ -331,6 +379,16 @@ int device_cu_count() {
   return n;
 }
 
+bool fused_quant_eligible(int64_t M, int64_t N, int64_t K) {
+  (void)N;
+  return M >= 1 && M <= 4 && M * K <= 65536;
+}
+
+size_t fused_quant_lds_bytes(int64_t M, int64_t K) {
+  const int64_t rows = M < 16 ? M : 16;
+  return (size_t)((rows * K + 15) / 16 * 16 + rows * (K / kGroup) * 4);
+}
+
 int auto_gemm_path(int64_t M, int64_t N) {
   // Up to one 64-row pass the streaming kernel is faster than any prefill tile on
   // every LLaMA-2-70B layer (M = 64, weights cold: qkv 37.5 vs 38.8 us, o 27 vs 37,
@@ -340,20 +398,23 @@ int auto_gemm_path(int64_t M, int64_t N) {
   return M <= kDecodeRowsPerPass ? 1 : 2;
 }
 
-template <int MT, int T, int S, int P, int C>
+template <int MT, int T, int S, int P, int C, bool FQ = false>
 static hipError_t launch_decode_c(const int8_t* qa, const float* sa, const uint32_t* wp,
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                   uint16_t* y, int64_t ntiles16, int64_t ntiles, int64_t items,
-                                  int64_t per_wg, int64_t grid, hipStream_t stream) {
-  return launch_kernel(gemm_decode_kernel<MT, T, S, P, C>, dim3((unsigned)grid), dim3(64 * S),
-                       stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, y, (int)ntiles16,
-                       (int)ntiles, (int)items, (int)per_wg);
+                                  int64_t per_wg, int64_t grid, hipStream_t stream,
+                                  const uint16_t* x = nullptr, int qmax = 0) {
+  const size_t lds_x = FQ ? fused_quant_lds_bytes(M, K) : 0;
+  return launch_kernel_lds(gemm_decode_kernel<MT, T, S, P, C, FQ>, dim3((unsigned)grid),
+                           dim3(64 * S), lds_x, stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, y,
+                           (int)ntiles16, (int)ntiles, (int)items, (int)per_wg, x, qmax);
 }
 
-template <int MT, int T, int S, int P, int CMAX>
+template <int MT, int T, int S, int P, int CMAX, bool FQ = false>
 static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint32_t* wp,
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
-                                  uint16_t* y, hipStream_t stream, bool chunk_few_rows = false) {
+                                  uint16_t* y, hipStream_t stream, bool chunk_few_rows = false,
+                                  const uint16_t* x = nullptr, int qmax = 0) {
   const int64_t ntiles16 = N / 16;
   const int64_t ntiles = (ntiles16 + T - 1) / T;
   const int64_t items = ntiles * ((M + 63) / 64);
@@ -366,19 +427,19 @@ static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint3
   // few token rows not worth the empty steps of a partial chunk, except where the
   // caller found it pays)
   if (M <= 4 && !chunk_few_rows)
-    return launch_decode_c<MT, T, S, P, 1>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items,
-                                           per_wg, grid, stream);
+    return launch_decode_c<MT, T, S, P, 1, FQ>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles,
+                                               items, per_wg, grid, stream, x, qmax);
   if (CMAX >= 8 && per_wg >= 5)
-    return launch_decode_c<MT, T, S, P, (CMAX >= 8 ? 8 : 1)>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items,
-                                           per_wg, grid, stream);
+    return launch_decode_c<MT, T, S, P, (CMAX >= 8 ? 8 : 1), FQ>(
+        qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items, per_wg, grid, stream, x, qmax);
   if (CMAX >= 4 && per_wg >= 3)
-    return launch_decode_c<MT, T, S, P, (CMAX >= 4 ? 4 : 1)>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items,
-                                           per_wg, grid, stream);
+    return launch_decode_c<MT, T, S, P, (CMAX >= 4 ? 4 : 1), FQ>(
+        qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items, per_wg, grid, stream, x, qmax);
   if (CMAX >= 2 && per_wg >= 2)
-    return launch_decode_c<MT, T, S, P, (CMAX >= 2 ? 2 : 1)>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items,
-                                           per_wg, grid, stream);
-  return launch_decode_c<MT, T, S, P, 1>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items,
-                                         per_wg, grid, stream);
+    return launch_decode_c<MT, T, S, P, (CMAX >= 2 ? 2 : 1), FQ>(
+        qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items, per_wg, grid, stream, x, qmax);
+  return launch_decode_c<MT, T, S, P, 1, FQ>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles,
+                                             items, per_wg, grid, stream, x, qmax);
 }
 
 hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t* wp,
@@ -419,6 +480,22 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
   }
   if (rows <= 48) return launch_decode_t<3, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
   return launch_decode_t<4, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
+}
+
+hipError_t launch_linear_decode_fused(const uint16_t* x, int64_t M, int64_t K, int qmax,
+                                      const uint32_t* wp, const uint16_t* sw, int64_t N,
+                                      uint16_t* y, hipStream_t stream) {
+  // the kernel configurations launch_gemm_decode takes for up to 4 rows
+  const int64_t cu = device_cu_count();
+  if (N / 16 <= 3 * cu && K <= 16384) {
+    if (N / 16 > 2 * cu)
+      return launch_decode_t<1, 2, 16, 2, 2, true>(nullptr, nullptr, wp, sw, M, N, K, y, stream,
+                                                   true, x, qmax);
+    return launch_decode_t<1, 1, 16, 2, 2, true>(nullptr, nullptr, wp, sw, M, N, K, y, stream,
+                                                 true, x, qmax);
+  }
+  return launch_decode_t<1, 2, 16, 2, 8, true>(nullptr, nullptr, wp, sw, M, N, K, y, stream,
+                                               false, x, qmax);
 }
 
 }  // namespace flexq

@@ -35,6 +35,31 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
                               const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                               hipStream_t stream);
 
+// launch_kernel with `lds_bytes` of dynamic LDS.
+template <typename... Params, typename... Args>
+hipError_t launch_kernel_lds(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds_bytes,
+                             hipStream_t stream, Args... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  std::tuple<Params...> values(static_cast<Params>(args)...);
+  void* ptrs[sizeof...(Params)];
+  std::apply([&ptrs](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, values);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds_bytes,
+                         stream);
+}
+
+// Activation quantization fused into the decode kernel: for up to 4 token rows with
+// rows * K <= 65536 each workgroup quantizes fp16 X into LDS (codes and scales
+// bit-identical to launch_quant_act) and streams the weights against it, so one
+// kernel does both steps.
+bool fused_quant_eligible(int64_t M, int64_t N, int64_t K);
+size_t fused_quant_lds_bytes(int64_t M, int64_t K);
+hipError_t launch_linear_decode_fused(const uint16_t* x, int64_t M, int64_t K, int qmax,
+                                      const uint32_t* wp, const uint16_t* sw, int64_t N,
+                                      uint16_t* y, hipStream_t stream);
+
 // Prefill tile shapes (rows x columns per workgroup); kTileAuto = prefill_tile(M, N).
 constexpr int kTileAuto = 0, kTile256x128 = 1, kTile128x128 = 2, kTile128x64 = 3;
 
@@ -47,6 +72,12 @@ int64_t prefill_main_cols(int64_t M, int64_t N);
 hipError_t launch_gemm_prefill(const int8_t* qa, const float* sa, const uint32_t* wp,
                                const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                                hipStream_t stream, int tile = kTileAuto);
+
+// The prefill kernel with loader and MFMA waves (256 x 128 tiles) over columns
+// n0 .. n0 + N - 1 of a product whose Y and s_w rows are ldn columns apart.
+hipError_t launch_gemm_prefill_ws(const int8_t* qa, const float* sa, const uint32_t* wp,
+                                  const uint16_t* sw, int64_t M, int64_t n0, int64_t N, int64_t K,
+                                  int64_t ldn, uint16_t* y, hipStream_t stream);
 
 hipError_t launch_group_dots(const int8_t* qa, const uint32_t* wp, int64_t M, int64_t N,
                              int64_t K, int32_t* dots, hipStream_t stream);
