@@ -4,8 +4,10 @@ A step is one pass of the hot path over one batch of synthetic input: for every
 token count M in {1, 16, 64, 256, 1024, 4096}, both activation precisions (A6, A8)
 and the four linear layers of a LLaMA-2-70B decoder block (qkv 10240x8192,
 o 8192x8192, gate_up 57344x8192, down 8192x28672), quantize the fp16 activations
-(flexq_quant_act) and run the W6Ax GEMM (flexq_gemm_w6ax) on packed 6-bit weights
-resident in HBM.  Weights are packed once, before timing (offline step).
+(flexq_quant_act) and run the W6Ax GEMM on packed 6-bit weights resident in HBM:
+flexq_gemm_w6ax with its automatic kernel choice, or flexq_gemm_w6ax_splitk in the
+planned configuration where flexq_gemm_w6ax_splitk_plan cuts K into slices (mid-sized
+M on the narrow layers).  Weights are packed once, before timing (offline step).
 
 Prints one JSON line: value = whole-step GEMM+quant throughput in TOPS (2*M*N*K
 integer ops per GEMM, M unpadded), per-shape TOPS / GB/s / roofline fractions,
@@ -130,6 +132,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def gemm_kind(fq, M, N, K):
+    """How the step runs one GEMM: ("splitk", S, tile path) where the split-K plan
+    cuts K, else ("decode",) or ("prefill",) as flexq_gemm_w6ax's automatic choice."""
+    S, tile = fq.splitk_plan(M, N, K)
+    if S > 1:
+        return ("splitk", S, tile)
+    return ("decode",) if fq.auto_path(M, N, K) == fq.PATH_DECODE else ("prefill",)
+
+
+def kernel_label(kind, M, N, K, fq):
+    if kind[0] == "splitk":
+        return f"splitk {TILE_NAMES[kind[2]]} x{kind[1]}"
+    if kind[0] == "decode":
+        return "decode"
+    return TILE_NAMES[fq.prefill_tile(M, N, K)] + ("+128x64" if fq.prefill_main_cols(M, N, K) < N
+                                                   else "")
+
+
 def summarize_trace(db, layers, m_list, reps):
     """Markdown summary of a rocprofv3 kernel-trace database (the `kernels` view of
     its SQLite output) of a bench run on `layers` at token counts `m_list`."""
@@ -150,7 +170,7 @@ def summarize_trace(db, layers, m_list, reps):
     # and grid (the tail split's two kernels per call both counted)
     grids = {}
     for name, dur, gx, wx in rows:
-        if "gemm_" in name:
+        if "gemm_" in name or "splitk_reduce" in name:
             g = grids.setdefault((name, gx // max(wx, 1)), [])
             g.append(dur)
     print("\n| kernel | workgroups | calls | avg (us) | min (us) | max (us) |\n|---|---|---|---|---|---|")
@@ -160,7 +180,8 @@ def summarize_trace(db, layers, m_list, reps):
               f"| {max(d) / 1e3:.2f} |")
     # The per-kernel runs of the bench, recognized in dispatch order: a busy kernel,
     # REPS_IN_RUN quantizer launches, then the GEMM launches of one (M, abits, layer)
-    # (two kernels per call where the prefill tail split applies); runs come in the
+    # (two kernels per call where the prefill tail split applies or split-K adds its
+    # reduce); runs come in the
     # bench's shape order, `steps` times over.
     ordered = con.execute("select name, duration from kernels order by start").fetchall()
     keys = sorted({(M, ab, n) for M in m_list for ab in ABITS for n in layers},
@@ -174,7 +195,8 @@ def summarize_trace(db, layers, m_list, reps):
                 j += 1
                 nq += 1
             g = []
-            while j < len(ordered) and "gemm_" in ordered[j][0]:
+            while j < len(ordered) and ("gemm_" in ordered[j][0] or
+                                        "splitk_reduce" in ordered[j][0]):
                 g.append(ordered[j][1])
                 j += 1
             if nq == reps and g:
@@ -194,12 +216,13 @@ def summarize_trace(db, layers, m_list, reps):
         M, ab, name = k
         N, K = layers[name]
         t = statistics.median(per_key[k])
-        dec = fq.auto_path(M, N, K) == fq.PATH_DECODE
-        print(f"| {name} | {M} | {ab} | {'decode' if dec else 'prefill'} | {t / 1e3:.2f} |")
+        kind = gemm_kind(fq, M, N, K)
+        dec = kind[0] == "decode"
+        print(f"| {name} | {M} | {ab} | {kernel_label(kind, M, N, K, fq)} | {t / 1e3:.2f} |")
         if dec and M <= 16:
             dec_b += gemm_bytes(M, N, K)
             dec_ns += t
-        if not dec:
+        if kind[0] == "prefill":
             pre_ops += 2.0 * M * N * K
             pre_ns += t
     if pre_ns:
@@ -285,7 +308,10 @@ def main():
             qa = torch.empty((M, K), dtype=torch.int8, device=dev)
             sa = torch.empty((K // GROUP, M), dtype=torch.float32, device=dev)
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
-            bufs[(M, name)] = (x, xd, qa, sa, y)
+            kind = gemm_kind(fq, M, N, K)
+            ws = (torch.empty(fq.splitk_workspace_bytes(M, N, K, kind[1]), dtype=torch.uint8,
+                              device=dev) if kind[0] == "splitk" else None)
+            bufs[(M, name)] = (x, xd, qa, sa, y, kind, ws)
     torch.cuda.synchronize()
     log(f"activations ready ({time.time() - t0:.1f} s)")
 
@@ -304,17 +330,26 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in plan]
 
+    def gemm(M, name, ab, wp, sw):
+        """One GEMM of the step, as gemm_kind says it runs."""
+        N, K = LAYERS[name]
+        _, _, qa, sa, y, kind, ws = bufs[(M, name)]
+        if kind[0] == "splitk":
+            fq.gemm_w6ax_splitk(qa, sa, wp, sw, N, ab, splits=kind[1], path=kind[2], y=y,
+                                workspace=ws)
+        else:
+            fq.gemm_w6ax(qa, sa, wp, sw, N, ab, y=y)
+
     def step(timed: bool):
         for i, (M, ab, name, widx) in enumerate(plan):
-            N, K = LAYERS[name]
-            _, xd, qa, sa, y = bufs[(M, name)]
+            _, xd, qa, sa, y = bufs[(M, name)][:5]
             wp, sw = packed[name][widx]
             if timed:
                 ev[i][0].record()
             fq.quant_act(xd, ab, q_a=qa, s_a=sa)
             if timed:
                 ev[i][1].record()
-            fq.gemm_w6ax(qa, sa, wp, sw, N, ab, y=y)
+            gemm(M, name, ab, wp, sw)
             if timed:
                 ev[i][2].record()
 
@@ -355,8 +390,7 @@ def main():
     for s in range(args.steps):
         for k in keys:
             M, ab, name = k
-            N, K = LAYERS[name]
-            _, xd, qa, sa, y = bufs[(M, name)]
+            _, xd, qa, sa, y = bufs[(M, name)][:5]
             cps = packed[name]
             fq.peak_mfma_i8(80000, 0, sink, clock)
             r0.record()
@@ -365,7 +399,7 @@ def main():
             r1.record()
             for j in range(REPS):
                 wp, sw = cps[(s * REPS + j) % len(cps)]
-                fq.gemm_w6ax(qa, sa, wp, sw, N, ab, y=y)
+                gemm(M, name, ab, wp, sw)
             r2.record()
             torch.cuda.synchronize()
             quant_ms[k].append(r0.elapsed_time(r1) / REPS)
@@ -402,8 +436,7 @@ def main():
 
     # ---- aggregate
     keys_by_m = sorted(keys, key=lambda k: (k[0], k[1], list(LAYERS).index(k[2])))
-    kernel_of = {k: ("decode" if fq.auto_path(k[0], *LAYERS[k[2]]) == fq.PATH_DECODE
-                     else "prefill") for k in keys}
+    kernel_of = {k: bufs[(k[0], k[2])][5][0] for k in keys}
     tot_ops = sum(2.0 * e[0] * LAYERS[e[2]][0] * LAYERS[e[2]][1] for e in plan)
     per_step = {k: len(step_gemm_ms[k]) // len(step_ms) for k in keys}
 
@@ -422,8 +455,7 @@ def main():
         ops = 2.0 * M * N * K
         by = gemm_bytes(M, N, K)
         dec = kernel_of[k] == "decode"
-        row = [name, M, ab, "decode" if dec else TILE_NAMES[fq.prefill_tile(M, N, K)]
-               + ("+128x64" if fq.prefill_main_cols(M, N, K) < N else ""),
+        row = [name, M, ab, kernel_label(bufs[(M, name)][5], M, N, K, fq),
                round(g * 1e3, 2), round(pct(gemm_ms[k], 0.1) * 1e3, 2),
                round(pct(gemm_ms[k], 0.9) * 1e3, 2),
                round(statistics.median(step_gemm_ms[k]) * 1e3, 2),
@@ -460,6 +492,7 @@ def main():
 
     dec_all = over(lambda M: True, "decode")
     pre_all = over(lambda M: True, "prefill")
+    split_all = over(lambda M: True, "splitk")
     dec16 = over(lambda M: M <= 16, "decode")
     pre1024 = over(lambda M: M >= 1024, "prefill")
     targets = {
@@ -526,7 +559,8 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.layers], "weight_copies": ncopies,
                    **({"stack_layers": STACK_LAYERS, "a8_layers": sorted(a8_layers)} if stack else {}),
                    "layers": {k: list(v) for k, v in LAYERS.items()}, "M": list(m_list),
-                   "abits": list(ABITS), "group": GROUP, "step": "quant_act + gemm per (M, abits, layer)"},
+                   "abits": list(ABITS), "group": GROUP,
+                   "step": "quant_act + gemm per (M, abits, layer); gemm = split-K where planned"},
         "roofline": roofline, "cpu_baseline": cpu,
         "launch": "hip_graph" if graph_ms else "eager",
         "ms_per_step_eager": round(ms_per_step_eager, 3),
@@ -538,6 +572,12 @@ def main():
         # last, where a truncated tail of the line still shows them
         "peaks": peaks, "roofline_decode": roofline_decode, "targets": targets,
     }
+    if split_all:
+        # the split-K launches (prefill kernel on K slices + the fixed-order reduce)
+        out["splitk"] = {"launches_per_step": sum(per_step[k] for k in keys
+                                                  if kernel_of[k] == "splitk"),
+                         "tops": round(split_all["tops"], 1), "gbs": round(split_all["gbs"], 1),
+                         "ms_per_step": round(split_all["ms"], 4)}
     print(json.dumps(out, separators=(",", ":")), flush=True)
 
 

@@ -167,6 +167,51 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a,
                                   int64_t M, int64_t N, int64_t K, int32_t group_size,
                                   int32_t abits, int32_t path, uint16_t* y_fp16, void* stream);
 
+/* Split-K form of the GEMM, for mid-sized M (tens to a few hundred tokens), where
+   the tile grid of the prefill kernel leaves compute units idle and each tile walks
+   all of K alone.  K is cut at group boundaries into S slices: slice s covers the
+   groups [s*G/S, (s+1)*G/S) (G = K/128) of every tile, in its own workgroup, and
+   accumulates them from +0 in ascending order with the preamble's t / fma steps into
+   fp32 plane s of the workspace ([S][M][N]).  A second kernel then adds the planes in
+   ascending s in fp32 and rounds once to fp16.  The integer group products are the
+   same as on every path; only the fp32 summation order differs from the preamble's
+   single ascending chain, so Y agrees with it to within one fp16 ulp, or else the
+   fp32 sum (acc_f32) agrees with the sequential accumulator to within 1e-5 times
+   sum_g |t * s_a| (the blog's "Bridging Software and Hardware with BTC" fixes the
+   exact integer group products and the fused dequantization, not an fp32 order).
+   With S = 1 the result is bit-identical to flexq_gemm_w6ax.  Deterministic: the
+   same inputs give the same bits on every call.
+     q_a, s_a, w_packed, s_w_fp16, y_fp16 as for flexq_gemm_w6ax
+     path      FLEXQ_PATH_PREFILL (the tile flexq_gemm_w6ax_splitk_plan reports) or
+               FLEXQ_PATH_PREFILL_256X128 / _128X128 / _128X64
+     splits    S, 1 <= S <= min(K/128, 64); 0 takes flexq_gemm_w6ax_splitk_plan's
+     workspace at least flexq_gemm_w6ax_splitk_workspace_bytes(M, N, K, S) bytes,
+               16-byte aligned, owned by the caller; overwritten, and not to be used
+               by other work until this call's kernels have run
+     acc_f32   NULL, or [M][N] fp32, 16-byte aligned: receives the fp32 sums that
+               Y rounds (for verification)
+   M == 0 or N == 0 is a no-op.  Errors: INVALID_VALUE (null, negative size, abits,
+   path, splits out of range, workspace too small, overlap of an output with an
+   input or of any two of workspace, y and acc), UNSUPPORTED (as for flexq_gemm_w6ax,
+   and M * N * S above 2^40 elements). */
+flexq_status flexq_gemm_w6ax_splitk(const int8_t* q_a, const float* s_a,
+                                    const uint32_t* w_packed, const uint16_t* s_w_fp16,
+                                    int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                    int32_t abits, int32_t path, int32_t splits,
+                                    void* workspace, size_t workspace_bytes, uint16_t* y_fp16,
+                                    float* acc_f32, void* stream);
+
+/* Bytes of workspace flexq_gemm_w6ax_splitk needs with `splits` slices (0 = the
+   planned count): splits * M * N * 4.  0 for M <= 0, N <= 0, K not a positive
+   multiple of 128 or splits outside 0 .. min(K/128, 64). */
+size_t flexq_gemm_w6ax_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t splits);
+
+/* The slice count S and tile (written to *tile_path when it is not NULL) that
+   flexq_gemm_w6ax_splitk takes for an M x N x K product on the current device when
+   asked to choose.  S = 1 means splitting is not expected to beat the tile grid
+   alone.  Never fails (degenerate shapes report 1 and FLEXQ_PATH_PREFILL_128X64). */
+int32_t flexq_gemm_w6ax_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t* tile_path);
+
 /* Bytes of workspace flexq_linear_w6ax needs for an M x K activation: q_a (M*K
    bytes, rounded up to a multiple of 256) followed by s_a (M*(K/128)*4 bytes).
    Returns 0 for M <= 0, K <= 0 or K not a multiple of 128. */

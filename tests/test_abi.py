@@ -377,3 +377,76 @@ def test_gemm_path_values(flexq):
         assert f(A16, 2 * A16, 3 * A16, 4 * A16, 4, 16, 128, 128, 6, bad, 5 * A16, None) == INVALID
     for p in range(7):  # every valid path with M = 0: a no-op
         assert f(None, None, 3 * A16, 4 * A16, 0, 16, 128, 128, 6, p, None, None) == SUCCESS
+
+
+def test_splitk_workspace_bytes(flexq):
+    f = flexq.flexq_gemm_w6ax_splitk_workspace_bytes
+    assert f(64, 10240, 8192, 2) == 2 * 64 * 10240 * 4
+    assert f(5, 16, 128, 1) == 5 * 16 * 4
+    assert f(64, 10240, 8192, 0) == 3 * 64 * 10240 * 4     # the plan's 3 slices
+    assert f(64, 10240, 8192, 64) == 64 * 64 * 10240 * 4   # K/128 = 64 slices at most
+    assert f(64, 10240, 8192, 65) == 0
+    assert f(64, 16, 256, 3) == 0                          # more slices than groups
+    assert f(0, 16, 128, 1) == 0 and f(4, 0, 128, 1) == 0 and f(4, 16, 100, 1) == 0
+    assert f(4, 16, 128, -1) == 0
+
+
+def test_splitk_rejects_bad_arguments(flexq):
+    f = flexq.flexq_gemm_w6ax_splitk
+    big = 1 << 32   # fake addresses 4 GiB apart
+    M, N, K = 8, 16, 256
+    need = flexq.flexq_gemm_w6ax_splitk_workspace_bytes(M, N, K, 2)
+
+    def call(M=M, N=N, K=K, group=128, abits=6, path=2, splits=2, qa=A16, sa=2 * A16,
+             wp=3 * A16, sw=4 * A16, ws=big, wb=need, y=2 * big, acc=3 * big):
+        return f(qa, sa, wp, sw, M, N, K, group, abits, path, splits, ws, wb, y, acc, None)
+
+    assert call(abits=7) == INVALID
+    for p in (0, 1, 6, 7, -1):
+        assert call(path=p) == INVALID
+    for p in (2, 3, 4, 5):
+        assert call(path=p, qa=None) == INVALID          # the path passes, the pointer not
+    assert call(splits=-1) == INVALID
+    assert call(splits=3) == INVALID                     # K = 256: at most 2 slices
+    assert call(K=128 * 80, splits=65) == INVALID        # 64 slices at most
+    assert call(qa=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(wb=need - 1) == INVALID                  # workspace too small
+    assert call(ws=big + 8) == UNSUPPORTED               # workspace not 16-byte aligned
+    assert call(acc=3 * big + 4) == UNSUPPORTED          # accumulator not 16-byte aligned
+    assert call(y=2 * big + 2) == UNSUPPORTED
+    assert call(K=200) == UNSUPPORTED
+    assert call(N=24) == UNSUPPORTED
+    assert call(group=64) == UNSUPPORTED
+    assert call(ws=A16) == INVALID                       # workspace overlaps q_a
+    assert call(ws=4 * A16) == INVALID                   # workspace overlaps s_w
+    assert call(acc=big + 64) == INVALID                 # accumulator overlaps the workspace
+    assert call(acc=2 * big) == INVALID                  # accumulator overlaps Y
+    assert call(acc=3 * A16) == INVALID                  # accumulator overlaps the weights
+    assert call(y=big) == INVALID                        # Y overlaps the workspace
+    assert call(M=0, qa=None, y=None, ws=None, wb=0) == SUCCESS
+    assert call(N=0, wp=None, y=None, ws=None, wb=0) == SUCCESS
+
+
+def test_splitk_plan_rule(flexq):
+    """The slice plan on the LLaMA-2-70B layers (256 CUs without a GPU): split on
+    narrow layers from 64 tokens up to a few hundred, never at 32 tokens or fewer,
+    never on gate_up (its grid of tiles already fills the GPU)."""
+    import w6a6_w6a8_integer_amd as fq
+    T256, T128 = fq.PATH_PREFILL_256X128, fq.PATH_PREFILL_128X128
+    L = {"qkv": (10240, 8192), "o": (8192, 8192), "gate_up": (57344, 8192), "down": (8192, 28672)}
+    expect = {("qkv", 64): (3, T128), ("qkv", 128): (3, T128), ("qkv", 256): (3, T256),
+              ("o", 64): (4, T128), ("o", 128): (4, T128), ("o", 256): (4, T256),
+              ("down", 64): (4, T128), ("down", 128): (4, T128), ("down", 256): (4, T256),
+              ("down", 512): (2, T256)}
+    for name, (N, K) in L.items():
+        for M in (1, 16, 32, 64, 128, 256, 512, 1024, 4096):
+            S, tile = fq.splitk_plan(M, N, K)
+            if (name, M) in expect:
+                assert (S, tile) == expect[(name, M)], (name, M, S, tile)
+            else:
+                assert S == 1, (name, M, S)
+                assert tile == fq.prefill_tile(M, N, K)
+    assert fq.splitk_plan(0, 16, 128) == (1, fq.PATH_PREFILL_128X64)
+    assert fq.splitk_plan(64, 16, 128)[0] == 1           # one group: nothing to split

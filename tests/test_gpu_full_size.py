@@ -14,7 +14,10 @@ Scope, for every layer of every workload:
   weight rows (four 16-row tiles) x every group, at every token count.
 
 Y is compared bit for bit: both kernels keep the sequential ascending-group fp32
-order of the definition.  At M <= 64 the one-call layer (flexq_linear_w6ax) must
+order of the definition.  Where the split-K plan cuts K into slices (mid-sized M on
+narrow layers), flexq_gemm_w6ax_splitk runs in the planned configuration too and its
+whole Y and fp32 accumulator are checked against the tolerance for a changed
+summation order (tests/tolerance.py).  At M <= 64 the one-call layer (flexq_linear_w6ax) must
 also give the two-call result in full.
 
 Workloads: the toy W6A6 layer, LLaMA-2-7B W6A6 (M 1/16/128), LLaMA-2-13B W6A8
@@ -32,6 +35,7 @@ import pytest
 
 import oracle
 import synth
+import tolerance
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -174,8 +178,10 @@ def test_full_size(fq, wname, lname):
                 d_got, d_ref, lambda b: (int(rows16[b[0]]), 16 * t0 + int(b[1]), int(b[2])))
 
             # Y
+            full = None   # the oracle's whole (Y, fp32 accumulator, S), computed once
             if M <= FULL_Y_MAX_M or wname in FULL_Y_WORKLOADS:
-                y_ref = oracle.gemm(qa_ref, sa_ref, qw, sw_ref, nthreads=THREADS)
+                full = oracle.gemm(qa_ref, sa_ref, qw, sw_ref, nthreads=THREADS, want_acc=True)
+                y_ref = full[0]
                 y_got = y.cpu().numpy().view(np.uint16)
                 assert np.array_equal(y_got, y_ref.view(np.uint16)), first_diffs(
                     y_got, y_ref.view(np.uint16), lambda b: (int(b[0]), int(b[1])))
@@ -202,5 +208,22 @@ def test_full_size(fq, wname, lname):
                 ref = np.array(list(_pool.map(one, range(PAIRS))), np.uint16)
                 assert np.array_equal(got, ref), first_diffs(
                     got, ref, lambda b: (int(pm[b[0]]), int(pn[b[0]])))
-            del y
+
+            # split-K where the plan splits (as the benchmark runs it): the whole Y and
+            # fp32 accumulator within the tolerance of the sequential definition
+            S_plan, tile = fq.splitk_plan(M, N, K)
+            if S_plan > 1:
+                say(f"{wname} {lname}: M={M} abits={abits}: split-K S={S_plan} tile path {tile}")
+                acc = torch.empty((M, N), dtype=torch.float32, device=DEV)
+                ys = fq.gemm_w6ax_splitk(qa, sa, wp, sw, N, abits, acc=acc)
+                torch.cuda.synchronize()
+                if full is None:
+                    full = oracle.gemm(qa_ref, sa_ref, qw, sw_ref, nthreads=THREADS,
+                                       want_acc=True)
+                ok, n_ulp, n_acc = tolerance.check(ys.cpu().numpy().view(np.uint16),
+                                                   full[0].view(np.uint16), acc.cpu().numpy(),
+                                                   full[1], full[2])
+                assert ok and n_acc == 0, (n_ulp, n_acc)
+                del ys, acc
+            del y, full
         del xd

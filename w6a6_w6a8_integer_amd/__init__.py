@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
 * :func:`gemm_w6ax`      Y[M][N] fp16 = sum over groups of int32 dot x s_w x s_a
 * :func:`linear_w6ax`    Y[M][N] fp16 from fp16 X in one call (both kernels, q_a / s_a
   in a caller-supplied or binding-allocated workspace)
+* :func:`gemm_w6ax_splitk` the GEMM with K split over workgroups (mid-sized M),
+  fp32 partials summed in a fixed order
 * :func:`gemm_w6ax_group_dots`  the int32 group dots (verification)
 """
 from __future__ import annotations
@@ -51,6 +53,10 @@ SIGNATURES = {
     "flexq_gemm_w6ax_auto_path": (ctypes.c_int, [_I64, _I64, _I64]),
     "flexq_gemm_w6ax_prefill_tile": (ctypes.c_int, [_I64, _I64, _I64]),
     "flexq_gemm_w6ax_prefill_main_cols": (ctypes.c_int64, [_I64, _I64, _I64]),
+    "flexq_gemm_w6ax_splitk": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32,
+                                              _I32, _I32, _P, ctypes.c_size_t, _P, _P, _P]),
+    "flexq_gemm_w6ax_splitk_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I32]),
+    "flexq_gemm_w6ax_splitk_plan": (ctypes.c_int32, [_I64, _I64, _I64, _P]),
     "flexq_linear_w6ax_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "flexq_linear_w6ax": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P,
                                          ctypes.c_size_t, _P, _P]),
@@ -227,6 +233,57 @@ def gemm_w6ax(q_a: torch.Tensor, s_a: torch.Tensor, w_packed: torch.Tensor, s_w:
     _check(lib().flexq_gemm_w6ax_path(q_a.data_ptr(), s_a.data_ptr(), w_packed.data_ptr(),
                                       s_w.data_ptr(), M, N, K, GROUP, abits, path, y.data_ptr(),
                                       _stream(q_a)), "flexq_gemm_w6ax")
+    return y
+
+
+def splitk_plan(M: int, N: int, K: int) -> tuple[int, int]:
+    """(S, tile path) that gemm_w6ax_splitk takes for this shape on the current
+    device when asked to choose (flexq_gemm_w6ax_splitk_plan)."""
+    tile = ctypes.c_int32(0)
+    S = int(lib().flexq_gemm_w6ax_splitk_plan(M, N, K, ctypes.byref(tile)))
+    return S, int(tile.value)
+
+
+def splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:
+    return int(lib().flexq_gemm_w6ax_splitk_workspace_bytes(M, N, K, splits))
+
+
+def gemm_w6ax_splitk(q_a: torch.Tensor, s_a: torch.Tensor, w_packed: torch.Tensor,
+                     s_w: torch.Tensor, N: int, abits: int, splits: int = 0,
+                     path: int = PATH_PREFILL, y: torch.Tensor | None = None,
+                     acc: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Split-K GEMM (flexq_gemm_w6ax_splitk): Y fp16[M][N] with K cut into `splits`
+    slices (0 = the planned count) whose fp32 partials are summed in ascending order;
+    `acc` (fp32[M][N], optional) receives the fp32 sums.  The workspace (uint8, at
+    least splitk_workspace_bytes(M, N, K, splits)) is allocated here when not passed."""
+    _matrix(q_a, torch.int8, "q_a")
+    M, K = q_a.shape
+    G = _groups(K, "gemm_w6ax_splitk")
+    N = _cols(N)
+    dev = q_a.device
+    _tensor(s_a, torch.float32, "s_a", shape=(G, M))
+    _packed(w_packed, N, K)
+    _tensor(s_w, torch.float16, "s_w", shape=(G, N))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    _tensor(y, torch.float16, "y", shape=(M, N))
+    if acc is not None:
+        _tensor(acc, torch.float32, "acc", shape=(M, N))
+    need = splitk_workspace_bytes(M, N, K, splits)
+    if workspace is None:
+        workspace = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+    if isinstance(workspace, torch.Tensor) and workspace.dim() != 1:
+        raise ValueError(f"workspace must be 1-D, got shape {tuple(workspace.shape)}")
+    _tensor(workspace, torch.uint8, "workspace", min_bytes=need)
+    tensors = dict(q_a=q_a, s_a=s_a, w_packed=w_packed, s_w=s_w, y=y, workspace=workspace)
+    if acc is not None:
+        tensors["acc"] = acc
+    _on_gpu(**tensors)
+    _check(lib().flexq_gemm_w6ax_splitk(q_a.data_ptr(), s_a.data_ptr(), w_packed.data_ptr(),
+                                        s_w.data_ptr(), M, N, K, GROUP, abits, path, splits,
+                                        workspace.data_ptr(), workspace.numel(), y.data_ptr(),
+                                        acc.data_ptr() if acc is not None else None,
+                                        _stream(q_a)), "flexq_gemm_w6ax_splitk")
     return y
 
 

@@ -5,6 +5,7 @@
 // the caller's stream and returns FLEXQ_SUCCESS (or FLEXQ_ERROR_LAUNCH if the runtime
 // rejected a launch).  No memory is allocated; the only global state is the
 // per-device compute-unit count that the launch geometry uses (gemm_decode.hip).
+#include <algorithm>
 #include <atomic>
 
 #include "../../include/flexq.h"
@@ -65,6 +66,21 @@ inline flexq_status check_m(int64_t M) {
 
 inline flexq_status launched(hipError_t e) {
   return e == hipSuccess ? FLEXQ_SUCCESS : FLEXQ_ERROR_LAUNCH;
+}
+
+// most K slices flexq_gemm_w6ax_splitk accepts
+constexpr int64_t kMaxSplits = 64;
+
+int path_of_tile(int tile) {
+  return tile == flexq::kTile256x128   ? FLEXQ_PATH_PREFILL_256X128
+         : tile == flexq::kTile128x128 ? FLEXQ_PATH_PREFILL_128X128
+                                       : FLEXQ_PATH_PREFILL_128X64;
+}
+
+int tile_of_path(int path) {
+  return path == FLEXQ_PATH_PREFILL_256X128   ? flexq::kTile256x128
+         : path == FLEXQ_PATH_PREFILL_128X128 ? flexq::kTile128x128
+                                              : flexq::kTile128x64;
 }
 
 #define FLEXQ_TRY(expr)                       \
@@ -261,6 +277,66 @@ flexq_status flexq_gemm_w6ax(const int8_t* q_a, const float* s_a, const uint32_t
                              int32_t group_size, int32_t abits, uint16_t* y_fp16, void* stream) {
   return flexq_gemm_w6ax_path(q_a, s_a, w_packed, s_w_fp16, M, N, K, group_size, abits,
                               FLEXQ_PATH_AUTO, y_fp16, stream);
+}
+
+int32_t flexq_gemm_w6ax_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t* tile_path) {
+  int tile = flexq::kTile128x64, S = 1;
+  if (M > 0 && N > 0 && K > 0 && K % kGroup == 0) flexq::splitk_plan(M, N, K, &tile, &S);
+  if (tile_path) *tile_path = path_of_tile(tile);
+  return S;
+}
+
+size_t flexq_gemm_w6ax_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t splits) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % kGroup != 0) return 0;
+  if (splits == 0) splits = flexq_gemm_w6ax_splitk_plan(M, N, K, nullptr);
+  if (splits < 1 || splits > std::min<int64_t>(K / kGroup, kMaxSplits)) return 0;
+  return (size_t)splits * (size_t)M * (size_t)N * 4;
+}
+
+flexq_status flexq_gemm_w6ax_splitk(const int8_t* q_a, const float* s_a, const uint32_t* w_packed,
+                                    const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K,
+                                    int32_t group_size, int32_t abits, int32_t path,
+                                    int32_t splits, void* workspace, size_t workspace_bytes,
+                                    uint16_t* y_fp16, float* acc_f32, void* stream) {
+  FLEXQ_TRY(check_m(M));
+  FLEXQ_TRY(check_n(N));
+  FLEXQ_TRY(check_k(K, group_size));
+  FLEXQ_TRY(check_scales(M, K));
+  FLEXQ_TRY(check_scales(N, K));
+  if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
+  if (path != FLEXQ_PATH_PREFILL && path != FLEXQ_PATH_PREFILL_256X128 &&
+      path != FLEXQ_PATH_PREFILL_128X128 && path != FLEXQ_PATH_PREFILL_128X64)
+    return FLEXQ_ERROR_INVALID_VALUE;
+  const int64_t G = K / kGroup;
+  if (splits < 0 || splits > std::min<int64_t>(G, kMaxSplits)) return FLEXQ_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return FLEXQ_SUCCESS;
+  int plan_tile = flexq::kTile128x64, plan_S = 1;
+  flexq::splitk_plan(M, N, K, &plan_tile, &plan_S);
+  const int S = splits == 0 ? plan_S : splits;
+  const int tile = path == FLEXQ_PATH_PREFILL ? plan_tile : tile_of_path(path);
+  if ((double)M * (double)N * (double)S > (double)(1LL << 40)) return FLEXQ_ERROR_UNSUPPORTED;
+  const uint64_t ws = (uint64_t)S * (uint64_t)M * (uint64_t)N * 4;
+  FLEXQ_TRY(validate_gemm_operands(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16,
+                                   (uint64_t)M * N * 2));
+  if (!workspace || workspace_bytes < ws) return FLEXQ_ERROR_INVALID_VALUE;
+  if (!aligned(workspace, 16) || (acc_f32 && !aligned(acc_f32, 16)))
+    return FLEXQ_ERROR_UNSUPPORTED;
+  const Range rw = range_of(workspace, ws), ry = range_of(y_fp16, (uint64_t)M * N * 2);
+  const Range inputs[4] = {range_of(q_a, (uint64_t)M * K), range_of(s_a, (uint64_t)M * G * 4),
+                           range_of(w_packed, (uint64_t)N * K * 3 / 4),
+                           range_of(s_w_fp16, (uint64_t)N * G * 2)};
+  for (const Range& in : inputs)
+    if (overlap(rw, in)) return FLEXQ_ERROR_INVALID_VALUE;
+  if (overlap(rw, ry)) return FLEXQ_ERROR_INVALID_VALUE;
+  if (acc_f32) {
+    const Range ra = range_of(acc_f32, (uint64_t)M * N * 4);
+    for (const Range& in : inputs)
+      if (overlap(ra, in)) return FLEXQ_ERROR_INVALID_VALUE;
+    if (overlap(ra, rw) || overlap(ra, ry)) return FLEXQ_ERROR_INVALID_VALUE;
+  }
+  return launched(flexq::launch_gemm_splitk(q_a, s_a, w_packed, s_w_fp16, M, N, K, tile, S,
+                                            static_cast<float*>(workspace), y_fp16, acc_f32,
+                                            (hipStream_t)stream));
 }
 
 size_t flexq_linear_w6ax_workspace_bytes(int64_t M, int64_t K) {

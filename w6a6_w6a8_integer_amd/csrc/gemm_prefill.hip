@@ -122,11 +122,16 @@ struct PrefillCfg {
   static constexpr int DMA_OPS = A_BLOCKS_PER_WAVE + 1;
 };
 
-template <int BM, int BN>
+// PARTIAL: split-K.  The grid is S times the tile grid; slice s of a tile takes the
+// groups [s*G/S, (s+1)*G/S) (G = K/128), accumulates them from +0 in ascending order
+// exactly as the whole product would, and stores its fp32 accumulators as plane s of
+// `part` ([S][M][ldn]) instead of fp16 Y.  The planes are summed afterwards in
+// ascending slice order (launch_splitk_reduce).
+template <int BM, int BN, bool PARTIAL>
 __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint32_t* __restrict__ wp,
     const uint16_t* __restrict__ sw, int M, int N, int K, int ldn, int GM,
-    uint16_t* __restrict__ y) {
+    uint16_t* __restrict__ y, int S, float* __restrict__ part) {
   using C = PrefillCfg<BM, BN>;
   constexpr int TN = C::TN;
   static_assert(TN == 1 || TN == 2, "one or two 32-column tiles per wave");
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   static_assert(C::B_UNITS * C::THREADS == BN * 8, "B split");
   static_assert(C::B_UNITS == 2 || C::B_UNITS == 4 || C::B_UNITS == 8, "unpack schedule");
 
-  const int G = K >> 7;
+  const int Gtot = K >> 7;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -144,9 +149,15 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
 
   // ---- logical tile from the workgroup id (XCD-contiguous, row-band order)
   const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
-  const int total = nbm * nbn;
+  const int tiles = nbm * nbn;
+  const int total = tiles * S;
   int pid = blockIdx.x;
   if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+  // K slice: groups g0 .. g0 + G - 1 (the whole of K when S = 1)
+  const int slice = pid / tiles;
+  pid -= slice * tiles;
+  const int g0 = (int)((int64_t)slice * Gtot / S);
+  const int G = (int)((int64_t)(slice + 1) * Gtot / S) - g0;
   const int band = GM * nbn;
   const int first_m = (pid / band) * GM;
   const int gm = min(GM, nbm - first_m);
@@ -164,8 +175,8 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   const auto rw = make_rsrc(wp + (size_t)(n0 / 16) * 3 * K, (uint32_t)(ncols / 16) * 12u * K);
   // scales are group-major: s_a[g][m] at g*M + m, s_w[g][n] at g*ldn + n (the launch
   // covers columns 0 .. N-1 of a matrix whose Y rows and s_w rows are ldn apart)
-  const auto rsa = make_rsrc(sa + m0, (uint32_t)((size_t)G * M - m0) * 4u);
-  const auto rsw = make_rsrc(sw + n0, (uint32_t)((size_t)(G - 1) * ldn + N - n0) * 2u);
+  const auto rsa = make_rsrc(sa + m0, (uint32_t)((size_t)Gtot * M - m0) * 4u);
+  const auto rsw = make_rsrc(sw + n0, (uint32_t)((size_t)(Gtot - 1) * ldn + N - n0) * 2u);
 
   // A stage: row-major, 128 bytes per row, the 16-byte chunk j of row r stored at
   // chunk j ^ ((r >> 1) & 7) (so the 32x32 fragment reads below touch every bank
@@ -226,13 +237,15 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
 
   // Prologue reads of group g: packed weights and weight scales into registers, then
   // activations and activation scales into the stage at byte offset `so`.
-  auto issue_regs = [&](int g, BRegs& r) {
+  auto issue_regs = [&](int gl, BRegs& r) {
+    const int g = g0 + gl;
 #pragma unroll
     for (int i = 0; i < C::B_UNITS; ++i)
       r.u[i] = __builtin_amdgcn_raw_buffer_load_b96(rw, b_voff_u[i], (uint32_t)g * 1536u, 0);
     r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)ldn * 2u, 0, 0);
   };
-  auto issue_dma = [&](int g, int so) {
+  auto issue_dma = [&](int gl, int so) {
+    const int g = g0 + gl;
     int8_t* la = lds + so;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -265,8 +278,9 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
   // the weight scale), so a group's reads can be spread over the MFMA steps: issued
   // in one burst by every wave right after a barrier, they queue at the texture unit
   // and stall the waves behind them.
-  auto vmem_op = [&](auto role, auto ic, int g, int so, BRegs& r) {
+  auto vmem_op = [&](auto role, auto ic, int gl, int so, BRegs& r) {
     constexpr int i = decltype(ic)::value;
+    const int g = g0 + gl;
     constexpr int kRole = decltype(role)::value;
     if constexpr (i < 4) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + so + (wave * 4 + i) * 1024),
@@ -525,6 +539,23 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     }, std::make_integer_sequence<int, 4>{});
   }
 
+  if constexpr (PARTIAL) {
+    // fp32 accumulators of this slice; lanes 0-31 and 32-63 of each store write 128
+    // contiguous bytes of two rows
+    float* pp = part + (size_t)slice * (size_t)M * (size_t)ldn;
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int col = wn * TN * 32 + tn * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + tm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row < mrows && col < ncols) pp[(size_t)(m0 + row) * ldn + n0 + col] = acc[tm][tn][r];
+        }
+      }
+    return;
+  }
   // Epilogue.  With a 16-byte aligned Y, each wave stages its 64 x 32TN fp16 outputs
   // in LDS (its own region, row pitch kOutPitch) and stores every row as 16-byte
   // chunks: 4TN store instructions per lane instead of 32TN two-byte ones.  The barrier
@@ -575,15 +606,22 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
 }
 
 // Columns n0 .. n0 + N - 1 of a product whose Y and s_w rows are ldn columns apart.
+// With part != nullptr: split-K into S slices, fp32 planes of [M][ldn] into part.
 template <int BM, int BN>
 static hipError_t launch_prefill_t(const int8_t* qa, const float* sa, const uint32_t* wp,
                                    const uint16_t* sw, int64_t M, int64_t n0, int64_t N,
-                                   int64_t K, int64_t ldn, uint16_t* y, hipStream_t stream) {
+                                   int64_t K, int64_t ldn, uint16_t* y, hipStream_t stream,
+                                   int S = 1, float* part = nullptr) {
   const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   const int GM = 4;
-  return launch_kernel(gemm_prefill_kernel<BM, BN>, dim3((unsigned)(nbm * nbn)), dim3(BM * 2),
-                       stream, qa, sa, wp + (n0 / 16) * 3 * K, sw + n0, (int)M, (int)N, (int)K,
-                       (int)ldn, GM, y + n0);
+  const dim3 grid((unsigned)(nbm * nbn * S)), block(BM * 2);
+  if (part != nullptr)
+    return launch_kernel(gemm_prefill_kernel<BM, BN, true>, grid, block, stream, qa, sa,
+                         wp + (n0 / 16) * 3 * K, sw + n0, (int)M, (int)N, (int)K, (int)ldn, GM,
+                         y, S, part + n0);
+  return launch_kernel(gemm_prefill_kernel<BM, BN, false>, grid, block, stream, qa, sa,
+                       wp + (n0 / 16) * 3 * K, sw + n0, (int)M, (int)N, (int)K, (int)ldn, GM,
+                       y + n0, 1, part);
 }
 
 static hipError_t launch_tile(int tile, const int8_t* qa, const float* sa, const uint32_t* wp,
@@ -594,6 +632,107 @@ static hipError_t launch_tile(int tile, const int8_t* qa, const float* sa, const
   if (tile == kTile128x128)
     return launch_prefill_t<128, 128>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
   return launch_prefill_t<128, 64>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
+}
+
+namespace {
+
+// Y = fp16(part[0] + part[1] + ... + part[S-1]) element by element, the planes added in
+// ascending order in fp32; acc (optional) receives the fp32 sums.  Four outputs per
+// thread and step (M * N is a multiple of 16).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S,
+                                                            int64_t n4, int64_t plane,
+                                                            uint16_t* __restrict__ y,
+                                                            float* __restrict__ acc) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(part + 4 * i);
+    for (int s = 1; s < S; ++s) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(part + (int64_t)s * plane + 4 * i);
+      a[0] += b[0];
+      a[1] += b[1];
+      a[2] += b[2];
+      a[3] += b[3];
+    }
+    if (acc != nullptr) *reinterpret_cast<f32x4*>(acc + 4 * i) = a;
+    uint32_t* y2 = reinterpret_cast<uint32_t*>(y) + 2 * i;
+    y2[0] = (uint32_t)float_to_half_bits(a[0]) | (uint32_t)float_to_half_bits(a[1]) << 16;
+    y2[1] = (uint32_t)float_to_half_bits(a[2]) | (uint32_t)float_to_half_bits(a[3]) << 16;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_splitk(const int8_t* qa, const float* sa, const uint32_t* wp,
+                              const uint16_t* sw, int64_t M, int64_t N, int64_t K, int tile,
+                              int S, float* part, uint16_t* y, float* acc, hipStream_t stream) {
+  hipError_t e;
+  if (tile == kTile256x128)
+    e = launch_prefill_t<256, 128>(qa, sa, wp, sw, M, 0, N, K, N, y, stream, S, part);
+  else if (tile == kTile128x128)
+    e = launch_prefill_t<128, 128>(qa, sa, wp, sw, M, 0, N, K, N, y, stream, S, part);
+  else if (tile == kTile128x64)
+    e = launch_prefill_t<128, 64>(qa, sa, wp, sw, M, 0, N, K, N, y, stream, S, part);
+  else
+    return hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
+  const int64_t n4 = M * N / 4;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, (int64_t)device_cu_count() * 8);
+  return launch_kernel(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), stream, part, S,
+                       n4, M * N, y, acc);
+}
+
+namespace {
+
+// Time model of one launch of the prefill kernel, in microseconds, fitted to
+// LLaMA-2-70B-shaped layers (M = 16 .. 512) on MI355X: the grid runs in rounds of
+// one workgroup per compute unit; a round costs a per-group time times the groups
+// each workgroup walks plus a fixed part; split-K adds the write and read of its fp32
+// planes (per MB of S * M * N * 4) and the reduce launch.  Median error 3 %.
+struct TileCost {
+  int tile, bm, bn;
+  double per_group, per_round, per_mb, fixed;
+};
+constexpr TileCost kCost[2] = {{kTile256x128, 256, 128, 1.108, 3.09, 0.362, 2.65},
+                               {kTile128x128, 128, 128, 0.784, 3.32, 0.324, 2.28}};
+
+double predict_us(const TileCost& c, int64_t M, int64_t N, int64_t G, int64_t S, int64_t cu,
+                  bool partial) {
+  const int64_t tiles = (M + c.bm - 1) / c.bm * ((N + c.bn - 1) / c.bn);
+  const int64_t rounds = (tiles * S + cu - 1) / cu;
+  const int64_t g = (G + S - 1) / S;
+  return (double)rounds * (c.per_group * (double)g + c.per_round) + c.fixed +
+         (partial ? c.per_mb * (double)(S * M * N * 4) / 1e6 : 0.0);
+}
+
+}  // namespace
+
+void splitk_plan(int64_t M, int64_t N, int64_t K, int* tile, int* S) {
+  const int64_t G = K / kGroup, cu = device_cu_count();
+  *tile = prefill_tile(M, N);
+  *S = 1;
+  // Few tokens: the weight-streaming kernel is faster, unless the layer is narrow
+  // (fewer than two 128 x 64 tiles per compute unit) and M is above 32.
+  if (M <= 32 || (M <= 64 && (M + 127) / 128 * ((N + 63) / 64) >= 2 * cu)) return;
+  double direct = 0.0;
+  for (const TileCost& c : kCost) {
+    const double t = predict_us(c, M, N, G, 1, cu, false);
+    if (direct == 0.0 || t < direct) direct = t;
+  }
+  double best = 0.0;
+  for (const TileCost& c : kCost)
+    for (int64_t s = 2; s <= std::min<int64_t>(G, 16); ++s) {
+      const double t = predict_us(c, M, N, G, s, cu, true);
+      if (best == 0.0 || t < best) {
+        best = t;
+        *tile = c.tile;
+        *S = (int)s;
+      }
+    }
+  // split only for a predicted gain of a tenth or more
+  if (best == 0.0 || best * 1.1 > direct) {
+    *tile = prefill_tile(M, N);
+    *S = 1;
+  }
 }
 
 int prefill_tile(int64_t M, int64_t N) {

@@ -73,6 +73,18 @@ hipError_t launch_gemm_prefill(const int8_t* qa, const float* sa, const uint32_t
                                const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                                hipStream_t stream, int tile = kTileAuto);
 
+// Split-K prefill: the tile grid times S workgroups, slice s accumulating groups
+// [s*G/S, (s+1)*G/S) (G = K/128) into fp32 plane s of part ([S][M][N]), then
+// Y = fp16(sum of the planes in ascending order), the fp32 sums also into acc when
+// it is not null.  tile is kTile256x128, kTile128x128 or kTile128x64; 1 <= S <= G.
+hipError_t launch_gemm_splitk(const int8_t* qa, const float* sa, const uint32_t* wp,
+                              const uint16_t* sw, int64_t M, int64_t N, int64_t K, int tile,
+                              int S, float* part, uint16_t* y, float* acc, hipStream_t stream);
+
+// The tile and slice count split-K takes for an M x N x K product on the current
+// device (S = 1 when splitting is not expected to pay).
+void splitk_plan(int64_t M, int64_t N, int64_t K, int* tile, int* S);
+
 // The prefill kernel with loader and MFMA waves (256 x 128 tiles) over columns
 // n0 .. n0 + N - 1 of a product whose Y and s_w rows are ldn columns apart.
 hipError_t launch_gemm_prefill_ws(const int8_t* qa, const float* sa, const uint32_t* wp,
