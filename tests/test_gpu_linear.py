@@ -1,6 +1,6 @@
 """GPU parity of flexq_linear_w6ax: one layer from fp16 activations in one call.
 
-For up to 4 rows with rows x K <= 65536 one kernel does both steps (each workgroup
+For up to 4 rows with rows x K <= 16384 one kernel does both steps (each workgroup
 quantizes X into LDS, then streams the weights); otherwise the activation quantizer
 and the GEMM run as two kernels with q_a and s_a in the caller's workspace.  Y must
 equal, bit for bit, the oracle's chain (quantize, then the group-quantized product)
@@ -57,9 +57,11 @@ SHAPES = [(1, 16, 128), (2, 48, 384), (3, 208, 2048), (4, 400, 2176), (1, 12304,
           (4, 12304, 384), (2, 64, 16512), (3, 1040, 1024), (5, 48, 1152), (40, 208, 1024),
           (300, 144, 768),
           # the fused quantizer's configurations and its limit: paired tiles on a
-          # narrow layer (more than 2 single tiles per CU), rows x K at 65536 exactly and
-          # one group past it (two kernels), the largest K it takes, a 70B qkv row
-          (2, 8320, 1024), (4, 64, 16384), (4, 64, 16512), (1, 64, 65536), (1, 10240, 8192)]
+          # narrow layer (more than 2 single tiles per CU), rows x K at 16384 exactly and
+          # one group past it (two kernels), the largest K it takes at one row and one
+          # group past that, a 70B qkv row
+          (2, 8320, 1024), (4, 64, 4096), (4, 64, 4224), (1, 64, 16384), (1, 64, 16512),
+          (1, 10240, 8192)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

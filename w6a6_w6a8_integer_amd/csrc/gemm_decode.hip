@@ -380,8 +380,13 @@ int device_cu_count() {
 }
 
 bool fused_quant_eligible(int64_t M, int64_t N, int64_t K) {
+  // Every workgroup quantizes all of X, so the prologue grows with M * K while the
+  // kernel boundary it saves is fixed.  In HIP graphs of 20 calls on the
+  // LLaMA-2-70B layers (us, fused / quant_act + GEMM): qkv M = 1, 2, 4: 15.6 / 17.7,
+  // 16.9 / 17.7, 19.3 / 18.0; o 12.4 / 13.7, 13.2 / 13.8, 15.8 / 14.2; gate_up M = 1
+  // 58.4 / 59.2, M = 2 57.5 / 57.0; down (K = 28672) M = 1 35.0 / 33.6.
   (void)N;
-  return M >= 1 && M <= 4 && M * K <= 65536;
+  return M >= 1 && M <= 4 && M * K <= 16384;
 }
 
 size_t fused_quant_lds_bytes(int64_t M, int64_t K) {

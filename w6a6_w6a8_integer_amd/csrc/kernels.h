@@ -51,7 +51,7 @@ hipError_t launch_kernel_lds(void (*kernel)(Params...), dim3 grid, dim3 block, s
 }
 
 // Activation quantization fused into the decode kernel: for up to 4 token rows with
-// rows * K <= 65536 each workgroup quantizes fp16 X into LDS (codes and scales
+// rows * K <= 16384 each workgroup quantizes fp16 X into LDS (codes and scales
 // bit-identical to launch_quant_act) and streams the weights against it, so one
 // kernel does both steps.
 bool fused_quant_eligible(int64_t M, int64_t N, int64_t K);
