@@ -175,7 +175,7 @@ def summarize_trace(db, layers, m_list, reps):
             g.append(dur)
     print("\n| kernel | workgroups | calls | avg (us) | min (us) | max (us) |\n|---|---|---|---|---|---|")
     for (name, wg), d in sorted(grids.items()):
-        short = name.split("(")[0].replace("void ", "")
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         print(f"| `{short}` | {wg} | {len(d)} | {sum(d) / len(d) / 1e3:.2f} | {min(d) / 1e3:.2f} "
               f"| {max(d) / 1e3:.2f} |")
     # The per-kernel runs of the bench, recognized in dispatch order: a busy kernel,
@@ -506,6 +506,8 @@ def main():
     if peaks and pre1024:
         targets["int8_frac_m_ge_1024_of_measured_mfma"] = round(
             pre1024["tops"] / peaks["mfma_i8_tops"], 4)
+        targets["int8_frac_m_ge_1024_of_rescale_loop"] = round(
+            pre1024["tops"] / peaks["rescale_loop_tops"], 4)
 
     pre_launches = sum(per_step[k] for k in keys if kernel_of[k] == "prefill")
     pre_kernels = sum(per_step[k] * (1 + (fq.prefill_main_cols(k[0], *LAYERS[k[2]]) <
@@ -527,6 +529,8 @@ def main():
         if peaks:
             roofline["measured_peak"] = round(peaks["mfma_i8_tops"], 1)
             roofline["frac_of_measured_peak"] = round(pre_all["tops"] / peaks["mfma_i8_tops"], 4)
+            roofline["rescale_loop_tops"] = peaks["rescale_loop_tops"]
+            roofline["frac_of_rescale_loop"] = round(pre_all["tops"] / peaks["rescale_loop_tops"], 4)
     else:
         roofline = {"kernel": "gemm_decode_kernel", "bound": "hbm",
                     "achieved": round(dec_all["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -586,7 +590,8 @@ def measure_peaks(fq, torch, dev, layers):
     a plain non-temporal read of each layer's packed-weight byte count and of 1 GiB
     (rotating over 3 buffers so no read is served from the MALL), and back-to-back
     int8 MFMAs with 0 and 8 independent FMAs per MFMA (8 = the fused rescale's count),
-    with the shader clock of the MFMA loop.  Medians of several launches."""
+    with the shader clock of the MFMA loop, and the exact rescale's instruction mix
+    without global memory (the rescale loop).  Medians of several launches."""
     sink = torch.empty(fq.peak_sink_bytes(), dtype=torch.uint8, device=dev)
     clock = torch.zeros(2, dtype=torch.int64, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -626,6 +631,15 @@ def measure_peaks(fq, torch, dev, layers):
         out[key + "_tops"] = round(ops / (ms * 1e-3) / 1e12, 1)
         out[key + "_clock_ghz"] = round(c[0] / c[1] * 0.1, 3)
     out["mfma_i8_valu8_frac_of_5pops"] = round(out["mfma_i8_valu8_tops"] / INT8_PEAK_TOPS, 4)
+    # the exact rescale's own instruction mix (chained MFMAs, 4 fma + 4 DPP fmac per
+    # MFMA, an LDS operand read per MFMA, a barrier per group): the ceiling of any
+    # kernel that keeps the two FMAs per output and group
+    iters = 2000
+    ops = fq.peak_mfma_i8_rescale(iters, sink, clock)
+    ms = timed(lambda: fq.peak_mfma_i8_rescale(iters, sink, clock), 5)
+    c = clock.cpu().tolist()
+    out["rescale_loop_tops"] = round(ops / (ms * 1e-3) / 1e12, 1)
+    out["rescale_loop_clock_ghz"] = round(c[0] / c[1] * 0.1, 3)
     props = torch.cuda.get_device_properties(dev)
     out["device"] = getattr(props, "gcnArchName", props.name)
     return out

@@ -4,7 +4,7 @@
  * against other systems, "What the Numbers Tell Us" in the blog "Meet FlexQ: A
  * Six-Bit Quantization Breakthrough"; these put the kernels against the hardware).
  *
- * Both calls enqueue one kernel on `stream` (a hipStream_t as void*, NULL = the null
+ * Each measurement enqueues one kernel on `stream` (a hipStream_t as void*, NULL = the null
  * stream) and return 0, or -1 for a bad argument (nothing enqueued), or -2 when the
  * runtime rejected the launch.  The caller times them (HIP events) and owns every
  * buffer.
@@ -19,7 +19,7 @@
 extern "C" {
 #endif
 
-/* Bytes the sink of both measurements must hold on the current device. */
+/* Bytes the sink of every measurement must hold on the current device. */
 size_t flexq_peak_sink_bytes(void);
 
 /* Plain streaming read: every 16-byte word of buf[0 .. bytes) is loaded once
@@ -43,6 +43,21 @@ int flexq_peak_mfma_i8(int64_t iters, int32_t valu_per_mfma, uint32_t* sink, uin
 
 /* Workgroups in the grid of flexq_peak_mfma_i8 on the current device (4 waves each). */
 int64_t flexq_peak_mfma_i8_workgroups(void);
+
+/* The instruction mix the exact group rescale sets a floor on (blog, "Bridging
+   Software and Hardware with BTC": the dequantization is fused into the GEMM, two
+   fp32 FMAs per output and group here), without global memory: one 512-thread
+   workgroup per compute unit (two waves per SIMD); per wave and round (one 128-deep
+   group) four 32 x 32 int8 tiles, each a chain of four v_mfma_i32_32x32x32_i8, the
+   previous tile's results rescaled under each chain (4 fma + 4 DPP-broadcast fmac
+   per MFMA, as in the prefill kernel), one 16-byte LDS read per MFMA, and one
+   workgroup barrier per round.  Ops per call = 2 * 32768 * 16 * iters * waves, with
+   waves = flexq_peak_mfma_i8_rescale_waves().  clock as for flexq_peak_mfma_i8;
+   iters in [1, 2^24]; sink of flexq_peak_sink_bytes() bytes (overwritten). */
+int flexq_peak_mfma_i8_rescale(int64_t iters, uint32_t* sink, uint64_t* clock, void* stream);
+
+/* Waves in the grid of flexq_peak_mfma_i8_rescale on the current device. */
+int64_t flexq_peak_mfma_i8_rescale_waves(void);
 
 #ifdef __cplusplus
 }

@@ -61,6 +61,10 @@ def test_peak_measurements_are_exported_and_check_arguments(flexq):
     assert flexq.flexq_peak_mfma_i8(0, 0, A16, 2 * A16, None) == -1
     assert flexq.flexq_peak_mfma_i8(10, 5, A16, 2 * A16, None) == -1
     assert flexq.flexq_peak_mfma_i8(10, 0, None, 2 * A16, None) == -1
+    assert flexq.flexq_peak_mfma_i8_rescale(0, A16, 2 * A16, None) == -1
+    assert flexq.flexq_peak_mfma_i8_rescale(1 << 25, A16, 2 * A16, None) == -1
+    assert flexq.flexq_peak_mfma_i8_rescale(10, A16, None, None) == -1
+    assert flexq.flexq_peak_mfma_i8_rescale_waves() == 256 * 8     # 256 CUs without a GPU
 
 
 def test_versions_and_status_strings(flexq):

@@ -69,6 +69,8 @@ PEAK_SIGNATURES = {
     "flexq_peak_hbm_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
     "flexq_peak_mfma_i8": (ctypes.c_int, [_I64, _I32, _P, _P, _P]),
     "flexq_peak_mfma_i8_workgroups": (ctypes.c_int64, []),
+    "flexq_peak_mfma_i8_rescale": (ctypes.c_int, [_I64, _P, _P, _P]),
+    "flexq_peak_mfma_i8_rescale_waves": (ctypes.c_int64, []),
 }
 # bytes of the library's per-GPU staging array behind flexq_linear_w6ax_noalloc
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -381,6 +383,18 @@ def peak_mfma_i8(iters: int, valu_per_mfma: int, sink: torch.Tensor,
     if rc != 0:
         raise RuntimeError(f"flexq_peak_mfma_i8 returned {rc}")
     return 2 * 32768 * 4 * iters * 4 * int(lib().flexq_peak_mfma_i8_workgroups())
+
+
+def peak_mfma_i8_rescale(iters: int, sink: torch.Tensor, clock: torch.Tensor) -> int:
+    """Enqueue flexq_peak_mfma_i8_rescale (int8 MFMA chains with the exact group
+    rescale, LDS operand reads and a barrier per group); returns the integer ops."""
+    _tensor(sink, torch.uint8, "sink", min_bytes=peak_sink_bytes())
+    _tensor(clock, torch.int64, "clock", shape=(2,))
+    _on_gpu(sink=sink, clock=clock)
+    rc = lib().flexq_peak_mfma_i8_rescale(iters, sink.data_ptr(), clock.data_ptr(), _stream(sink))
+    if rc != 0:
+        raise RuntimeError(f"flexq_peak_mfma_i8_rescale returned {rc}")
+    return 2 * 32768 * 16 * iters * int(lib().flexq_peak_mfma_i8_rescale_waves())
 
 
 def peak_sink_bytes() -> int:
