@@ -54,7 +54,7 @@ M_LIST = (1, 16, 64, 256, 1024, 4096)
 ABITS = (6, 8)
 
 
-TILE_NAMES = {3: "256x128", 4: "128x128", 5: "128x64"}
+TILE_NAMES = {3: "256x128", 4: "128x128", 5: "128x64", 7: "64x128"}
 REPS_IN_RUN = 20   # back-to-back launches per timed run of one shape
 
 

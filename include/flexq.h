@@ -86,7 +86,10 @@ typedef enum {
   FLEXQ_PATH_PREFILL_128X128 = 4,
   FLEXQ_PATH_PREFILL_128X64 = 5,
   /* 256 x 128 tiles computed by 4 MFMA waves while 4 loader waves stage the operands */
-  FLEXQ_PATH_PREFILL_256X128_WS = 6
+  FLEXQ_PATH_PREFILL_256X128_WS = 6,
+  /* the prefill kernel with 64 x 128 tiles (two waves, two workgroups per compute
+     unit), for few tokens on wide layers */
+  FLEXQ_PATH_PREFILL_64X128 = 7
 } flexq_path;
 
 #define FLEXQ_ABI_VERSION 1
@@ -138,17 +141,20 @@ flexq_status flexq_gemm_w6ax(const int8_t* q_a, const float* s_a, const uint32_t
                              int32_t group_size, int32_t abits, uint16_t* y_fp16, void* stream);
 
 /* The kernel FLEXQ_PATH_AUTO runs for an M x N x K product: FLEXQ_PATH_DECODE (the
-   weight-streaming kernel) for M <= FLEXQ_DECODE_MAX_M, FLEXQ_PATH_PREFILL above.
-   N and K do not enter the choice.  Never fails (M <= 0 or N <= 0 report
+   weight-streaming kernel) for M <= FLEXQ_DECODE_MAX_M, FLEXQ_PATH_PREFILL above,
+   and also for 48 <= M <= FLEXQ_DECODE_MAX_M where flexq_gemm_w6ax_prefill_tile
+   reports the 64 x 128 tile (a layer at least 1.5 * 128 columns wide per compute
+   unit).  K does not enter the choice.  Never fails (M <= 0 or N <= 0 report
    FLEXQ_PATH_DECODE). */
 int flexq_gemm_w6ax_auto_path(int64_t M, int64_t N, int64_t K);
 
 /* The tile FLEXQ_PATH_PREFILL uses for an M x N x K product on the current device
-   (one of FLEXQ_PATH_PREFILL_256X128 / _128X128 / _128X64): the 256 x 128 tile when
-   the grid of 128 x 128 tiles needs enough more rounds of one tile per compute unit
-   (rounds256 * 1.46 < rounds128), else 128 x 64 when 128 x 128 tiles would number
-   no more than the compute units, else 128 x 128.  K does not enter the choice.
-   Never fails. */
+   (one of FLEXQ_PATH_PREFILL_256X128 / _128X128 / _128X64 / _64X128): 64 x 128 for
+   M <= 64 when the 128-column tiles number at least 1.5 per compute unit; otherwise
+   the 256 x 128 tile when the grid of 128 x 128 tiles needs enough more rounds of one
+   tile per compute unit (rounds256 * 1.46 < rounds128), else 128 x 64 when 128 x 128
+   tiles would number no more than the compute units, else 128 x 128.  K does not
+   enter the choice.  Never fails. */
 int flexq_gemm_w6ax_prefill_tile(int64_t M, int64_t N, int64_t K);
 
 /* Tail split of FLEXQ_PATH_PREFILL.  When the 256 x 128 grid ends in a partly filled
@@ -183,7 +189,7 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a,
    same inputs give the same bits on every call.
      q_a, s_a, w_packed, s_w_fp16, y_fp16 as for flexq_gemm_w6ax
      path      FLEXQ_PATH_PREFILL (the tile flexq_gemm_w6ax_splitk_plan reports) or
-               FLEXQ_PATH_PREFILL_256X128 / _128X128 / _128X64
+               FLEXQ_PATH_PREFILL_256X128 / _128X128 / _128X64 / _64X128
      splits    S, 1 <= S <= min(K/128, 64); 0 takes flexq_gemm_w6ax_splitk_plan's
      workspace at least flexq_gemm_w6ax_splitk_workspace_bytes(M, N, K, S) bytes,
                16-byte aligned, owned by the caller; overwritten, and not to be used

@@ -139,7 +139,7 @@ def test_gemm_rejects_bad_arguments(flexq):
     assert call(y=3 * A16 + 32) == INVALID  # Y overlaps the packed weight
     assert call(M=0, qa=None, y=None) == SUCCESS
     assert call(N=0, wp=None, y=None) == SUCCESS
-    assert g(A16, 2 * A16, 3 * A16, 4 * A16, 4, 16, 128, 128, 6, 7, 5 * A16, None) == INVALID
+    assert g(A16, 2 * A16, 3 * A16, 4 * A16, 4, 16, 128, 128, 6, 8, 5 * A16, None) == INVALID
 
 
 def test_group_dots_rejects_bad_arguments(flexq):
@@ -312,16 +312,22 @@ def test_binding_checks_the_other_entry_points():
 
 
 def test_auto_path_rule(flexq):
-    """The automatic kernel choice as flexq.h states it: the streaming kernel up to
-    one 64-row pass, the tiled kernel above, whatever the layer's width."""
+    """The automatic kernel choice as flexq.h states it (256 CUs without a GPU): the
+    streaming kernel up to one 64-row pass, the tiled kernel above; from 48 rows the
+    tiled kernel also where the 64 x 128 tile's grid fills the GPU (at least 384
+    128-column tiles)."""
     import w6a6_w6a8_integer_amd as fq
     DEC, PRE = fq.PATH_DECODE, fq.PATH_PREFILL
     assert fq.auto_path(1, 57344, 8192) == DEC
     assert fq.auto_path(32, 57344, 8192) == DEC
-    assert fq.auto_path(48, 57344, 8192) == DEC
-    assert fq.auto_path(64, 10240, 8192) == DEC
-    assert fq.auto_path(64, 57344, 8192) == DEC
-    assert fq.auto_path(64, 1 << 24, 128) == DEC
+    assert fq.auto_path(47, 57344, 8192) == DEC
+    assert fq.auto_path(48, 57344, 8192) == PRE       # 448 column tiles
+    assert fq.auto_path(64, 57344, 8192) == PRE
+    assert fq.auto_path(64, 10240, 8192) == DEC       # 80 column tiles
+    assert fq.auto_path(64, 49152, 8192) == PRE       # 384: the boundary
+    assert fq.auto_path(64, 49136, 8192) == PRE       # 384 tiles, the last one ragged
+    assert fq.auto_path(64, 49024, 8192) == DEC       # 383
+    assert fq.auto_path(64, 1 << 24, 128) == PRE
     assert fq.auto_path(65, 16, 128) == PRE
     assert fq.auto_path(65, 57344, 8192) == PRE
     assert fq.auto_path(4096, 16, 128) == PRE
@@ -332,6 +338,7 @@ def test_prefill_tile_rule(flexq):
     """The prefill tile choice as flexq.h states it (256 CUs without a GPU)."""
     import w6a6_w6a8_integer_amd as fq
     T256, T128, T64 = fq.PATH_PREFILL_256X128, fq.PATH_PREFILL_128X128, fq.PATH_PREFILL_128X64
+    T64R = fq.PATH_PREFILL_64X128
     # LLaMA-2-70B layers
     assert fq.prefill_tile(4096, 57344, 8192) == T256    # 7168 vs 14336 tiles
     assert fq.prefill_tile(1024, 8192, 8192) == T256     # 1 round vs 2
@@ -341,7 +348,9 @@ def test_prefill_tile_rule(flexq):
     assert fq.prefill_tile(512, 8192, 8192) == T64       # 256 <= 256: one round either way
     assert fq.prefill_tile(512, 10240, 8192) == T256     # 1 round vs 2
     assert fq.prefill_tile(256, 57344, 8192) == T256     # 2 rounds vs 4
-    assert fq.prefill_tile(64, 57344, 8192) == T128      # 448 tiles: 2 rounds either way
+    assert fq.prefill_tile(64, 57344, 8192) == T64R      # 448 column tiles >= 1.5 per CU
+    assert fq.prefill_tile(65, 57344, 8192) == T128      # two 64-row blocks: 128-row tiles
+    assert fq.prefill_tile(16, 49024, 8192) == T128      # 383 column tiles: the 128-row rule
     # the boundary between the narrow and the square tile
     assert fq.prefill_tile(128, 32768, 256) == T64       # 256 tiles of 128 x 128
     assert fq.prefill_tile(128, 32784, 256) == T128      # 257
@@ -377,9 +386,9 @@ def test_prefill_tail_split_rule(flexq):
 
 def test_gemm_path_values(flexq):
     f = flexq.flexq_gemm_w6ax_path
-    for bad in (-1, 7, 8):
+    for bad in (-1, 8, 9):
         assert f(A16, 2 * A16, 3 * A16, 4 * A16, 4, 16, 128, 128, 6, bad, 5 * A16, None) == INVALID
-    for p in range(7):  # every valid path with M = 0: a no-op
+    for p in range(8):  # every valid path with M = 0: a no-op
         assert f(None, None, 3 * A16, 4 * A16, 0, 16, 128, 128, 6, p, None, None) == SUCCESS
 
 
@@ -406,9 +415,9 @@ def test_splitk_rejects_bad_arguments(flexq):
         return f(qa, sa, wp, sw, M, N, K, group, abits, path, splits, ws, wb, y, acc, None)
 
     assert call(abits=7) == INVALID
-    for p in (0, 1, 6, 7, -1):
+    for p in (0, 1, 6, 8, -1):
         assert call(path=p) == INVALID
-    for p in (2, 3, 4, 5):
+    for p in (2, 3, 4, 5, 7):
         assert call(path=p, qa=None) == INVALID          # the path passes, the pointer not
     assert call(splits=-1) == INVALID
     assert call(splits=3) == INVALID                     # K = 256: at most 2 slices

@@ -21,10 +21,11 @@ pytestmark = [pytest.mark.gpu,
 DEV = "cuda:0"
 G = 128
 # (M, N, K, abits, path): decode (1, 16, 40 rows); prefill by the automatic choice
-# (128 x 64 tiles at these sizes) and by name with 256 x 128 and 128 x 128 tiles
+# (128 x 64 tiles at these sizes) and by name with 256 x 128, 128 x 128 and 64 x 128
+# tiles
 CASES = [(1, 512, 1024, 6, 0), (16, 1040, 2048, 8, 0), (40, 208, 1024, 6, 0),
          (300, 400, 768, 8, 0), (1100, 144, 384, 6, 0), (300, 400, 768, 6, 3),
-         (1100, 144, 384, 8, 4)]
+         (1100, 144, 384, 8, 4), (60, 400, 1152, 8, 7)]
 LINEAR_CASES = [(2, 400, 1024, 8), (8, 208, 768, 6)]
 
 

@@ -50,7 +50,7 @@ def test_maximum_k(fq, abits):
     assert np.array_equal(qa.cpu().numpy(), qa_ref)
     assert np.array_equal(sa.cpu().numpy().T.view(np.uint32), sa_ref.view(np.uint32))
     for path in (fq.PATH_DECODE, fq.PATH_PREFILL_256X128, fq.PATH_PREFILL_128X128,
-                 fq.PATH_PREFILL_128X64, fq.PATH_PREFILL_256X128_WS):
+                 fq.PATH_PREFILL_128X64, fq.PATH_PREFILL_256X128_WS, fq.PATH_PREFILL_64X128):
         say(f"K = 2^22 abits={abits} path={path}")
         y = fq.gemm_w6ax(qa, sa, wp, sw, N, abits, path=path)
         assert np.array_equal(y.cpu().numpy().view(np.uint16), y_ref), f"path {path}"

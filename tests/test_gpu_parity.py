@@ -218,9 +218,9 @@ SHAPES = [(16, 256, 512), (1, 16, 128), (5, 48, 1152), (17, 272, 640), (33, 160,
           (300, 16368, 256), (256, 16384, 256), (1024, 8192, 256)]
 
 
-@pytest.mark.parametrize("path", [1, 2, 3, 4, 5, 6],
+@pytest.mark.parametrize("path", [1, 2, 3, 4, 5, 6, 7],
                          ids=["decode", "prefill", "tile256x128", "tile128x128", "tile128x64",
-                              "tile256x128ws"])
+                              "tile256x128ws", "tile64x128"])
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_gemm_bit_exact_every_path(fq, M, N, K, path):
     say(f"gemm M={M} N={N} K={K} path={path}")
@@ -240,7 +240,7 @@ def test_gemm_zero_rows_and_zero_groups(fq):
     x[5, G:2 * G] = 0
     w[7] = 0
     w[9, :G] = 0
-    for path in (1, 3, 4, 5, 6):   # decode, then each prefill tile
+    for path in (1, 3, 4, 5, 6, 7):   # decode, then each prefill tile
         qa, sa = oracle.quant_act(x, 6)
         wp, sw = oracle.pack_w6(w)
         y_ref = oracle.gemm_packed(qa, sa, wp, sw, N)
@@ -257,7 +257,7 @@ def test_gemm_deterministic_and_in_bounds(fq):
     qa, sa = oracle.quant_act(x, 8)
     wp, sw = oracle.pack_w6(w)
     args = (to_dev(qa), to_dev(gm(sa)), to_dev(wp.view(np.int32)), to_dev(gm(sw)))
-    for path in (1, 3, 4, 5, 6):   # decode, then each prefill tile
+    for path in (1, 3, 4, 5, 6, 7):   # decode, then each prefill tile
         buf = torch.full((M * N + 4096,), -1, dtype=torch.int16, device=DEV)
         y = buf[:M * N].view(torch.float16).view(M, N)
         fq.gemm_w6ax(*args, N, 8, y=y, path=path)
@@ -278,7 +278,7 @@ def test_gemm_output_not_16_byte_aligned(fq, M, N, K):
     wp, sw = oracle.pack_w6(w)
     y_ref = oracle.gemm_packed(qa, sa, wp, sw, N).view(np.uint16)
     args = (to_dev(qa), to_dev(gm(sa)), to_dev(wp.view(np.int32)), to_dev(gm(sw)))
-    for path in (1, 3, 4, 5, 6):   # decode, then each prefill tile
+    for path in (1, 3, 4, 5, 6, 7):   # decode, then each prefill tile
         buf = torch.full((M * N + 4096,), -1, dtype=torch.int16, device=DEV)
         y = buf[2:2 + M * N].view(torch.float16).view(M, N)   # 4 bytes past a 16-byte boundary
         assert y.data_ptr() % 16 == 4

@@ -6,8 +6,9 @@ Each case draws M in 1..320 (decode passes of 16/32/48/64 rows, prefill row tile
 counts for single and paired decode tiles and for 64- and 128-wide prefill tiles),
 K a multiple of 128 in 128..3072 (group counts below, at and past the 16 a decode
 workgroup folds per round and the 6 a prefill loop unrolls), the activation
-precision and the path (automatic, decode, automatic prefill tile, or one named
-tile).  Y and the activation codes and scales must equal the oracle's bit for bit.
+precision and the path (automatic, decode, automatic prefill tile, one named tile,
+the warp-specialized kernel or the 64 x 128 tile).  Y and the activation codes and
+scales must equal the oracle's bit for bit.
 """
 import numpy as np
 import pytest
@@ -33,7 +34,7 @@ def draw_cases():
         N = 16 * int(rng.integers(1, 129))
         K = G * int(rng.integers(1, 25))
         abits = int(rng.choice([6, 8]))
-        path = int(rng.integers(0, 6))
+        path = int(rng.integers(0, 8))
         cases.append((i, M, N, K, abits, path))
     return cases
 

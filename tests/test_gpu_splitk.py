@@ -5,7 +5,7 @@ K is cut into S slices at group boundaries; each slice accumulates its groups fr
 ascending order.  So:
 
 * S = 1 is the definition itself: Y and the fp32 accumulator bit for bit, on every
-  tile (256 x 128, 128 x 128, 128 x 64);
+  tile (256 x 128, 128 x 128, 128 x 64, 64 x 128);
 * S > 1 changes only the fp32 summation order: every output within one fp16 ulp or
   its fp32 sum within 1e-5 * sum |t * s_a| of the sequential accumulator (the
   tolerance module), and in these cases every fp32 sum within that bound;
@@ -31,7 +31,7 @@ DEV = "cuda:0"
 # (M, N, K)
 SHAPES = [(64, 256, 1024), (100, 144, 1280), (257, 272, 2048), (1, 16, 128), (130, 64, 384),
           (37, 400, 2816)]
-TILES = (3, 4, 5)   # PATH_PREFILL_256X128, _128X128, _128X64
+TILES = (3, 4, 5, 7)   # PATH_PREFILL_256X128, _128X128, _128X64, _64X128
 
 
 @pytest.fixture(scope="module")

@@ -34,6 +34,8 @@ PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 PATH_PREFILL_256X128, PATH_PREFILL_128X128, PATH_PREFILL_128X64 = 3, 4, 5
 # 256 x 128 tiles from 4 MFMA waves with 4 loader waves staging the operands
 PATH_PREFILL_256X128_WS = 6
+# the prefill kernel with 64 x 128 tiles (few tokens on wide layers)
+PATH_PREFILL_64X128 = 7
 
 STATUS_NAMES = {0: "FLEXQ_SUCCESS", 1: "FLEXQ_ERROR_INVALID_VALUE", 2: "FLEXQ_ERROR_UNSUPPORTED",
                 3: "FLEXQ_ERROR_LAUNCH"}

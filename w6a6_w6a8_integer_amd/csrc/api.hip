@@ -74,13 +74,17 @@ constexpr int64_t kMaxSplits = 64;
 int path_of_tile(int tile) {
   return tile == flexq::kTile256x128   ? FLEXQ_PATH_PREFILL_256X128
          : tile == flexq::kTile128x128 ? FLEXQ_PATH_PREFILL_128X128
+         : tile == flexq::kTile64x128  ? FLEXQ_PATH_PREFILL_64X128
                                        : FLEXQ_PATH_PREFILL_128X64;
 }
 
+// the tile of a fixed-tile prefill path (kTileAuto for FLEXQ_PATH_PREFILL)
 int tile_of_path(int path) {
   return path == FLEXQ_PATH_PREFILL_256X128   ? flexq::kTile256x128
          : path == FLEXQ_PATH_PREFILL_128X128 ? flexq::kTile128x128
-                                              : flexq::kTile128x64;
+         : path == FLEXQ_PATH_PREFILL_128X64  ? flexq::kTile128x64
+         : path == FLEXQ_PATH_PREFILL_64X128  ? flexq::kTile64x128
+                                              : flexq::kTileAuto;
 }
 
 #define FLEXQ_TRY(expr)                       \
@@ -231,7 +235,7 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a, const uin
   FLEXQ_TRY(check_scales(M, K));
   FLEXQ_TRY(check_scales(N, K));
   if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
-  if (path < FLEXQ_PATH_AUTO || path > FLEXQ_PATH_PREFILL_256X128_WS)
+  if (path < FLEXQ_PATH_AUTO || path > FLEXQ_PATH_PREFILL_64X128)
     return FLEXQ_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return FLEXQ_SUCCESS;
   FLEXQ_TRY(validate_gemm_operands(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16,
@@ -243,10 +247,7 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a, const uin
   if (path == FLEXQ_PATH_PREFILL_256X128_WS)
     return launched(
         flexq::launch_gemm_prefill_ws(q_a, s_a, w_packed, s_w_fp16, M, 0, N, K, N, y_fp16, s));
-  const int tile = path == FLEXQ_PATH_PREFILL_256X128   ? flexq::kTile256x128
-                   : path == FLEXQ_PATH_PREFILL_128X128 ? flexq::kTile128x128
-                   : path == FLEXQ_PATH_PREFILL_128X64  ? flexq::kTile128x64
-                                                        : flexq::kTileAuto;
+  const int tile = tile_of_path(path);
   return launched(
       flexq::launch_gemm_prefill(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s, tile));
 }
@@ -254,10 +255,7 @@ flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a, const uin
 int flexq_gemm_w6ax_prefill_tile(int64_t M, int64_t N, int64_t K) {
   (void)K;
   if (M <= 0 || N <= 0) return FLEXQ_PATH_PREFILL_128X64;
-  const int t = flexq::prefill_tile(M, N);
-  return t == flexq::kTile256x128   ? FLEXQ_PATH_PREFILL_256X128
-         : t == flexq::kTile128x128 ? FLEXQ_PATH_PREFILL_128X128
-                                    : FLEXQ_PATH_PREFILL_128X64;
+  return path_of_tile(flexq::prefill_tile(M, N));
 }
 
 int64_t flexq_gemm_w6ax_prefill_main_cols(int64_t M, int64_t N, int64_t K) {
@@ -305,7 +303,8 @@ flexq_status flexq_gemm_w6ax_splitk(const int8_t* q_a, const float* s_a, const u
   FLEXQ_TRY(check_scales(N, K));
   if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
   if (path != FLEXQ_PATH_PREFILL && path != FLEXQ_PATH_PREFILL_256X128 &&
-      path != FLEXQ_PATH_PREFILL_128X128 && path != FLEXQ_PATH_PREFILL_128X64)
+      path != FLEXQ_PATH_PREFILL_128X128 && path != FLEXQ_PATH_PREFILL_128X64 &&
+      path != FLEXQ_PATH_PREFILL_64X128)
     return FLEXQ_ERROR_INVALID_VALUE;
   const int64_t G = K / kGroup;
   if (splits < 0 || splits > std::min<int64_t>(G, kMaxSplits)) return FLEXQ_ERROR_INVALID_VALUE;

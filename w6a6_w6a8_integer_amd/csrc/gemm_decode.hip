@@ -395,12 +395,15 @@ size_t fused_quant_lds_bytes(int64_t M, int64_t K) {
 }
 
 int auto_gemm_path(int64_t M, int64_t N) {
-  // Up to one 64-row pass the streaming kernel is faster than any prefill tile on
-  // every LLaMA-2-70B layer (M = 64, weights cold: qkv 37.5 vs 38.8 us, o 27 vs 37,
-  // gate_up 108 vs 121, down 87 vs 127); beyond it the weights would be streamed
-  // once per 64 rows and the tiled kernel wins.
-  (void)N;
-  return M <= kDecodeRowsPerPass ? 1 : 2;
+  // Up to one 64-row pass the streaming kernel is faster than the 128-row prefill
+  // tiles on every LLaMA-2-70B layer (M = 64, weights cold: qkv 37.5 vs 38.8 us, o 27
+  // vs 37, gate_up 108 vs 121, down 87 vs 127); beyond it the weights would be
+  // streamed once per 64 rows and the tiled kernel wins.  From 48 rows on wide
+  // layers, where the 64 x 128 tile's grid fills the GPU (prefill_tile), that tile
+  // wins instead: gate_up M = 64 96 -> 78 us, M = 48 79 -> 76 us (it loses at 32 rows
+  // and below, and on narrow layers, whose grids it leaves half empty).
+  if (M > kDecodeRowsPerPass) return 2;
+  return M >= 48 && prefill_tile(M, N) == kTile64x128 ? 2 : 1;
 }
 
 template <int MT, int T, int S, int P, int C, bool FQ = false>

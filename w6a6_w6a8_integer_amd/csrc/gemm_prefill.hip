@@ -61,9 +61,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int STAGES = 3;
-constexpr int kOutPitch = 144;
-// which scale vector a wave loads in the main loop
-constexpr int kRoleNone = 0, kRoleSa = 1, kRoleSw = 2;  // bytes per staged output row: 128 + 16 of padding
+constexpr int kOutPitch = 144;  // bytes per staged output row: 128 + 16 of padding
+// which scale vectors a wave loads in the main loop (both: the 64-row tile, whose one
+// activation-scale wave also covers half the weight scales)
+constexpr int kRoleNone = 0, kRoleSa = 1, kRoleSw = 2, kRoleBoth = 3;
 
 // s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
 // vmcnt[5:4] in [15:14]).
@@ -207,13 +208,16 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     a_voff[i] = a_vrow + (uint32_t)(i * 8) * (uint32_t)K +
                 (uint32_t)(((lane & 7) ^ (4 * (i & 1) + (lane >> 4))) * 16);
   // Scales: in the main loop only waves 0 .. SA_WAVES-1 copy s_a (64 rows each) and
-  // only the next BN/64 waves load s_w (one column per thread); each global load
-  // instruction costs issue time whatever its size, so no wave loads a copy another
-  // wave already brings.  The main loop exists once per role (kRoleSa, kRoleSw,
+  // only BN/64 waves load s_w (one column per thread): the next ones, or with two
+  // waves (the 64-row tile) both, the first doing both; each global load instruction
+  // costs issue time whatever its size, so no wave loads a copy another wave already
+  // brings.  The main loop exists once per role (kRoleSa, kRoleSw, kRoleBoth,
   // kRoleNone) so that no branch splits it.  (The prologue loads the scales in every
   // wave; duplicates write identical values.)
+  constexpr int SW0 = C::SA_WAVES < C::WAVES - BN / 64 ? C::SA_WAVES : C::WAVES - BN / 64;
+  static_assert(SW0 >= 0, "enough waves for the weight scales");
   const bool sa_wave = wave < C::SA_WAVES;
-  const bool sw_wave = wave >= C::SA_WAVES && wave < C::SA_WAVES + BN / 64;
+  const bool sw_wave = wave >= SW0 && wave < SW0 + BN / 64;
   const int sa_row0 = (wave % C::SA_WAVES) * 64;
   const uint32_t sa_voff = (uint32_t)(sa_row0 + lane) * 4u;
   // B: wave w loads the 16-column tiles TPW*w .. TPW*w + TPW - 1 of the group
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + so + (wave * 4 + i) * 1024),
                                                16, a_voff[i], (uint32_t)g * 128u, 0, 0);
     } else if constexpr (i == 4) {
-      if constexpr (kRole == kRoleSa)
+      if constexpr (kRole == kRoleSa || kRole == kRoleBoth)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsa, (lds_ptr_t)(lds + so + C::A_BYTES + C::B_BYTES + sa_row0 * 4), 4,
             sa_voff + (uint32_t)g * (uint32_t)M * 4u, 0, 0, 0);
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
       r.u[i - 5] = __builtin_amdgcn_raw_buffer_load_b96(rw, b_voff_u[i - 5], (uint32_t)g * 1536u,
                                                         0);
     } else {
-      if constexpr (kRole == kRoleSw)
+      if constexpr (kRole == kRoleSw || kRole == kRoleBoth)
         r.s = __builtin_amdgcn_raw_buffer_load_b16(rsw, sw_voff + (uint32_t)g * (uint32_t)ldn * 2u,
                                                    0, 0);
     }
@@ -483,7 +487,8 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
         if constexpr (k == 1 + (u * (STEPS - 2)) / C::B_UNITS) fill_unit(so_next, other, u);
       }, std::make_integer_sequence<int, C::B_UNITS>{});
       if constexpr (k == STEPS - 1) {
-        if constexpr (decltype(role)::value == kRoleSw) fill_scale(so_next, other);
+        if constexpr (decltype(role)::value == kRoleSw || decltype(role)::value == kRoleBoth)
+          fill_scale(so_next, other);
       }
       if constexpr (TN == 2) step_order();
       __builtin_amdgcn_sched_barrier(0);
@@ -539,12 +544,19 @@ __global__ __launch_bounds__(BM * 2, 1) void gemm_prefill_kernel(
     }
     if (g < G) step_group(role, g, so, so1, so2, breg[0], breg[1]);
   };
-  if (sa_wave)
-    main_loop(std::integral_constant<int, kRoleSa>{});
-  else if (sw_wave)
-    main_loop(std::integral_constant<int, kRoleSw>{});
-  else
-    main_loop(std::integral_constant<int, kRoleNone>{});
+  if constexpr (SW0 < C::SA_WAVES) {  // the 64-row tile: wave 0 both, wave 1 s_w
+    if (sa_wave)
+      main_loop(std::integral_constant<int, kRoleBoth>{});
+    else
+      main_loop(std::integral_constant<int, kRoleSw>{});
+  } else {
+    if (sa_wave)
+      main_loop(std::integral_constant<int, kRoleSa>{});
+    else if (sw_wave)
+      main_loop(std::integral_constant<int, kRoleSw>{});
+    else
+      main_loop(std::integral_constant<int, kRoleNone>{});
+  }
   wait_vm_lgkm0<0>();  // no copy into LDS may outlive the workgroup
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
@@ -647,6 +659,8 @@ static hipError_t launch_tile(int tile, const int8_t* qa, const float* sa, const
     return launch_prefill_t<256, 128>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
   if (tile == kTile128x128)
     return launch_prefill_t<128, 128>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
+  if (tile == kTile64x128)
+    return launch_prefill_t<64, 128>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
   return launch_prefill_t<128, 64>(qa, sa, wp, sw, M, n0, N, K, ldn, y, stream);
 }
 
@@ -688,6 +702,8 @@ hipError_t launch_gemm_splitk(const int8_t* qa, const float* sa, const uint32_t*
     e = launch_prefill_t<128, 128>(qa, sa, wp, sw, M, 0, N, K, N, y, stream, S, part);
   else if (tile == kTile128x64)
     e = launch_prefill_t<128, 64>(qa, sa, wp, sw, M, 0, N, K, N, y, stream, S, part);
+  else if (tile == kTile64x128)
+    e = launch_prefill_t<64, 128>(qa, sa, wp, sw, M, 0, N, K, N, y, stream, S, part);
   else
     return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
@@ -762,6 +778,10 @@ int prefill_tile(int64_t M, int64_t N) {
   // M = 64 ... 512: 25-30 % faster on o and down).
   const int64_t cu = device_cu_count();
   const int64_t nbn = (N + 127) / 128;
+  // One 64-row block on a wide layer: 64 x 128 tiles waste no rows, and two share a
+  // compute unit, so from 1.5 column tiles per CU their grid fills the GPU (70B
+  // gate_up at M = 64: 78 us against 111-113 us for the 128-row tiles).
+  if (M <= 64 && nbn * 2 >= 3 * cu) return kTile64x128;
   const int64_t tiles128 = (M + 127) / 128 * nbn;
   const int64_t rounds256 = ((M + 255) / 256 * nbn + cu - 1) / cu;
   const int64_t rounds128 = (tiles128 + cu - 1) / cu;
@@ -803,7 +823,7 @@ hipError_t launch_gemm_prefill(const int8_t* qa, const float* sa, const uint32_t
     if (e != hipSuccess || n_main == N) return e;
     return launch_tile(kTile128x64, qa, sa, wp, sw, M, n_main, N - n_main, K, N, y, stream);
   }
-  if (tile != kTile256x128 && tile != kTile128x128 && tile != kTile128x64)
+  if (tile != kTile256x128 && tile != kTile128x128 && tile != kTile128x64 && tile != kTile64x128)
     return hipErrorInvalidValue;
   return launch_tile(tile, qa, sa, wp, sw, M, 0, N, K, N, y, stream);
 }

@@ -61,7 +61,8 @@ hipError_t launch_linear_decode_fused(const uint16_t* x, int64_t M, int64_t K, i
                                       uint16_t* y, hipStream_t stream);
 
 // Prefill tile shapes (rows x columns per workgroup); kTileAuto = prefill_tile(M, N).
-constexpr int kTileAuto = 0, kTile256x128 = 1, kTile128x128 = 2, kTile128x64 = 3;
+constexpr int kTileAuto = 0, kTile256x128 = 1, kTile128x128 = 2, kTile128x64 = 3,
+              kTile64x128 = 4;
 
 // The tile the prefill kernel uses for an M x N product on the current device.
 int prefill_tile(int64_t M, int64_t N);
@@ -76,7 +77,8 @@ hipError_t launch_gemm_prefill(const int8_t* qa, const float* sa, const uint32_t
 // Split-K prefill: the tile grid times S workgroups, slice s accumulating groups
 // [s*G/S, (s+1)*G/S) (G = K/128) into fp32 plane s of part ([S][M][N]), then
 // Y = fp16(sum of the planes in ascending order), the fp32 sums also into acc when
-// it is not null.  tile is kTile256x128, kTile128x128 or kTile128x64; 1 <= S <= G.
+// it is not null.  tile is kTile256x128, kTile128x128, kTile128x64 or kTile64x128;
+// 1 <= S <= G.
 hipError_t launch_gemm_splitk(const int8_t* qa, const float* sa, const uint32_t* wp,
                               const uint16_t* sw, int64_t M, int64_t N, int64_t K, int tile,
                               int S, float* part, uint16_t* y, float* acc, hipStream_t stream);
