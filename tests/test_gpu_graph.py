@@ -108,3 +108,57 @@ def test_graph_replays_match_eager(fq):
         for i, ((*_, y), yr) in enumerate(zip(lin, lin_ref)):
             assert torch.equal(y.view(torch.int16), yr.view(torch.int16)), \
                 f"replay {rep} linear case {LINEAR_CASES[i]}"
+
+
+def test_splitk_graph_replays_match_eager(fq):
+    """The split-K GEMM (slice kernel + ordered reduce) captured in a HIP graph, as the
+    benchmark captures it: every replay, between eager work that poisons Y, the
+    accumulator and the workspace, gives the eager bits, and those are within the
+    tolerance of the oracle."""
+    import tolerance
+    cases = [(64, 1024, 4096, 8, 0, 2), (130, 400, 1280, 6, 3, 3), (60, 400, 1152, 6, 4, 7)]
+    bufs = []
+    for i, (M, N, K, abits, splits, path) in enumerate(cases):
+        path = path if path >= 3 else fq.PATH_PREFILL
+        x = synth.activations(synth.derive_seed(23, "x", i), M, K)
+        w = synth.weights(synth.derive_seed(23, "w", i), N, K)
+        qa_ref, sa_ref = oracle.quant_act(x, abits)
+        wp_ref, sw_ref = oracle.pack_w6(w)
+        ref = oracle.gemm_packed(qa_ref, sa_ref, wp_ref, sw_ref, N, want_acc=True)
+        dev = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+               for a in (qa_ref, sa_ref.T, wp_ref.view(np.int32), sw_ref.T)]
+        ws = torch.empty(max(16, fq.splitk_workspace_bytes(M, N, K, splits)), dtype=torch.uint8,
+                         device=DEV)
+        y = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        acc = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        bufs.append((M, N, K, abits, splits, path, dev, ws, y, acc, ref))
+
+    def run():
+        for (M, N, K, abits, splits, path, dev, ws, y, acc, _) in bufs:
+            fq.gemm_w6ax_splitk(*dev, N, abits, splits=splits, path=path, y=y, acc=acc,
+                                workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [(y.clone(), acc.clone()) for (*_, y, acc, _) in bufs]
+    for (M, N, K, abits, splits, path, dev, ws, y, acc, ref), (ye, ae) in zip(bufs, eager):
+        ok, _, n_acc = tolerance.check(ye.cpu().numpy().view(np.uint16), ref[0].view(np.uint16),
+                                       ae.cpu().numpy(), ref[1], ref[2])
+        assert ok and n_acc == 0, (M, N, K, splits, path)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for (*_, ws, y, acc, _) in bufs:
+            y.fill_(float("nan"))
+            acc.fill_(float("nan"))
+            ws.fill_(0xCD)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, ((*_, y, acc, _), (ye, ae)) in enumerate(zip(bufs, eager)):
+            assert torch.equal(y.view(torch.int16), ye.view(torch.int16)), f"replay {rep} case {i}: y"
+            assert torch.equal(acc.view(torch.int32), ae.view(torch.int32)), \
+                f"replay {rep} case {i}: acc"
