@@ -1,11 +1,12 @@
 """GPU parity under concurrent host threads: the C ABI called from several threads at
 once, each thread enqueueing on a stream of its own (default priority).
 
-Four threads start together and each runs one layer 16 times, alternating the
-one-call path (flexq_linear_w6ax, binding-allocated workspace) and the two-call
-path (flexq_quant_act, then flexq_gemm_w6ax), and querying the automatic path and
-the prefill tile before every call, so the per-device compute-unit cache is first
-filled while the other threads use it.  The layers cover the decode kernel (1, 16
+Four threads start together and each runs one layer 16 times, rotating through the
+one-call path (flexq_linear_w6ax, binding-allocated workspace), the two-call path
+(flexq_quant_act, then flexq_gemm_w6ax) and the split-K GEMM with one slice (its
+own workspace), and querying the automatic path, the prefill tile and the split-K
+plan before every call, so the per-device compute-unit cache is first filled while
+the other threads use it.  The layers cover the decode kernel (1, 16
 and 40 rows) and the prefill kernel (300 rows), A6 and A8.  Every output must equal
 the oracle's bit for bit.
 """
@@ -61,11 +62,16 @@ def test_concurrent_threads_bit_exact(fq):
                 for it in range(ITERS):
                     fq.auto_path(M, N, K)
                     fq.prefill_tile(M, N, K)
-                    if it % 2 == 0:
+                    fq.splitk_plan(M, N, K)
+                    if it % 3 == 0:
                         outs.append(fq.linear_w6ax(x, wp, sw, N, abits))
-                    else:
+                    elif it % 3 == 1:
                         qa, sa = fq.quant_act(x, abits)
                         outs.append(fq.gemm_w6ax(qa, sa, wp, sw, N, abits))
+                    else:  # split-K with one slice: the definition, bit for bit
+                        qa, sa = fq.quant_act(x, abits)
+                        outs.append(fq.gemm_w6ax_splitk(qa, sa, wp, sw, N, abits, splits=1,
+                                                        path=fq.PATH_PREFILL_128X64))
             stream.synchronize()
             results[i] = [o.cpu().numpy().view(np.uint16) for o in outs]
         except Exception as e:  # reported by the main thread
