@@ -54,6 +54,8 @@ def _load():
         "oracle_unpack_codes": (ctypes.c_int, [_P, _I64, _I64, _P]),
         "oracle_pack_w6": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
         "oracle_quant_act": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
+        "oracle_pack_act_a6": (ctypes.c_int, [_P, _I64, _I64, _P]),
+        "oracle_unpack_act_a6": (ctypes.c_int, [_P, _I64, _I64, _P]),
         "oracle_group_dots": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_int]),
         "oracle_gemm": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P,
                                        ctypes.c_int]),
@@ -173,6 +175,26 @@ def quant_act(x: np.ndarray, abits: int, group: int = GROUP):
     _check(_load().oracle_quant_act(x.ctypes.data, M, K, group, abits, qa.ctypes.data,
                                     sa.ctypes.data), "quant_act")
     return qa, sa
+
+
+def pack_act_a6(qa: np.ndarray) -> np.ndarray:
+    """Codes qa int8 [M][K] (each in [-32, 31]) -> uint32 [M][3*K/16]: 16 codes per
+    3-dword unit (the packed-weight unit), the units of a row in order."""
+    qa = _c(qa, np.int8)
+    M, K = qa.shape
+    qp = np.zeros((M, 3 * K // 16), np.uint32)
+    _check(_load().oracle_pack_act_a6(qa.ctypes.data, M, K, qp.ctypes.data), "pack_act_a6")
+    return qp
+
+
+def unpack_act_a6(qp: np.ndarray, K: int) -> np.ndarray:
+    """uint32 [M][3*K/16] -> codes int8 [M][K]."""
+    qp = _c(qp, np.uint32)
+    M = qp.shape[0]
+    assert qp.shape == (M, 3 * K // 16)
+    qa = np.empty((M, K), np.int8)
+    _check(_load().oracle_unpack_act_a6(qp.ctypes.data, M, K, qa.ctypes.data), "unpack_act_a6")
+    return qa
 
 
 # --- products -----------------------------------------------------------------

@@ -239,6 +239,31 @@ int oracle_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t group, int
 }
 
 /* ------------------------------------------------------------------------- */
+/* 6-bit activation storage                                                   */
+/* FlexQ abstract: W6A6, so activations can be held at 6 bits.  The same      */
+/* 16-code unit as the packed weights, laid out row by row: unit u of token   */
+/* row m at dword 3 * (m * K/16 + u).                                         */
+/* ------------------------------------------------------------------------- */
+
+int oracle_pack_act_a6(const int8_t* qa, int64_t M, int64_t K, uint32_t* qp) {
+  if (!qa || !qp || M <= 0 || K <= 0 || K % 16) return -1;
+  for (int64_t i = 0; i < M * K; ++i)
+    if (qa[i] < -32 || qa[i] > 31) return -3;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t u = 0; u < K / 16; ++u)
+      oracle_pack_unit(qa + m * K + u * 16, qp + 3 * (m * (K / 16) + u));
+  return 0;
+}
+
+int oracle_unpack_act_a6(const uint32_t* qp, int64_t M, int64_t K, int8_t* qa) {
+  if (!qa || !qp || M <= 0 || K <= 0 || K % 16) return -1;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t u = 0; u < K / 16; ++u)
+      oracle_unpack_unit(qp + 3 * (m * (K / 16) + u), qa + m * K + u * 16);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Integer group dots and the fused-dequantization accumulation               */
 /* Blog "Bridging ... BTC": exact integer partial products per K-group, then  */
 /* dequantization fused into the accumulation.                                */

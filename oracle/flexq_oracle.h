@@ -59,6 +59,14 @@ int oracle_pack_w6(const uint16_t* w, int64_t N, int64_t K, int64_t group,
 int oracle_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t group, int abits,
                      int8_t* qa, float* sa);
 
+/* 6-bit activation storage (FlexQ abstract: W6A6, activations held at 6 bits): the
+   codes qa [M][K] (each in [-32, 31], else -3) packed 16 per unit as above, the
+   units of a token row one after another: unit u = k/16 of row m at dword
+   3 * (m * K/16 + u), 0.75 * K bytes per row.  K % 16 == 0. */
+int oracle_pack_act_a6(const int8_t* qa, int64_t M, int64_t K, uint32_t* qp);
+/* Decode qp back into codes [M][K]. */
+int oracle_unpack_act_a6(const uint32_t* qp, int64_t M, int64_t K, int8_t* qa);
+
 /* Integer group dot products d[m][n][g] = sum over k in group g of qa[m][k]*qw[n][k]. */
 int oracle_group_dots(const int8_t* qa, const int8_t* qw, int64_t M, int64_t N, int64_t K,
                       int64_t group, int32_t* dots, int nthreads);

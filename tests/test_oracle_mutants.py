@@ -36,6 +36,10 @@ MUTANTS = [
     ("scale_not_rounded_to_fp16", "sf = oracle_f16_to_f32(s16);", "sf = s;"),
     ("tile_minor_major_swapped", "return 3 * (((n / 16) * units_per_row + u) * 16 + (n % 16));",
      "return 3 * (((n / 16) * 16 + (n % 16)) * units_per_row + u);"),
+    ("act_a6_units_column_major", "oracle_pack_unit(qa + m * K + u * 16, qp + 3 * (m * (K / 16) + u));",
+     "oracle_pack_unit(qa + m * K + u * 16, qp + 3 * (u * M + m));"),
+    ("act_a6_accepts_8bit_codes", "if (qa[i] < -32 || qa[i] > 31) return -3;",
+     "if (qa[i] < -128 || qa[i] > 127) return -3;"),
 ]
 
 PIN_TESTS = [
@@ -56,6 +60,9 @@ PIN_TESTS = [
     (pins.test_gemm_within_fp32_bound_of_fp64_brute_force, {"abits": 8}),
     (pins.test_gemm_accumulation_in_exact_rationals, {}),
     (pins.test_gemm_power_of_two_scales_are_exact, {}),
+    (pins.test_pack_act_a6_golden_units_in_row_order, {}),
+    (pins.test_pack_act_a6_is_the_weight_unit_grid_transposed, {}),
+    (pins.test_pack_act_a6_round_trip_and_range, {}),
 ]
 
 

@@ -133,6 +133,72 @@ def test_pack_codes_matrix_round_trip():
 
 
 # ---------------------------------------------------------------------------
+# 6-bit activation storage: the packed unit, row by row
+# ---------------------------------------------------------------------------
+
+def test_pack_act_a6_golden_units_in_row_order():
+    """A 2 x 48 code matrix built from the hand-derived units: unit u of row m is
+    golden line (3m + u) % 6 and must sit, as those three words, at dword
+    3 * (3m + u) (row-major units, 0.75 K bytes per row)."""
+    units = _golden_units()
+    M, K = 2, 48
+    qa = np.zeros((M, K), np.int8)
+    for m in range(M):
+        for u in range(K // 16):
+            qa[m, 16 * u:16 * u + 16] = units[(3 * m + u) % len(units)][0]
+    qp = oracle.pack_act_a6(qa)
+    assert qp.shape == (M, 3 * K // 16) and qp.nbytes == M * K * 3 // 4
+    flat = qp.reshape(-1)
+    for m in range(M):
+        for u in range(K // 16):
+            words = units[(3 * m + u) % len(units)][1]
+            assert [int(w) for w in flat[3 * (3 * m + u):3 * (3 * m + u) + 3]] == words
+    assert np.array_equal(oracle.unpack_act_a6(qp, K), qa)
+
+
+def test_pack_act_a6_is_the_weight_unit_grid_transposed():
+    """For one 16-row block the packed weights (pinned above) hold unit (n, u) at
+    unit index 16u + n; the activation layout holds unit (m, u) at m * K/16 + u:
+    the same units, the grid transposed."""
+    rng = np.random.default_rng(11)
+    K = 384
+    q = rng.integers(-32, 32, (16, K)).astype(np.int8)
+    act = oracle.pack_act_a6(q).reshape(16, K // 16, 3)
+    wts = oracle.pack_codes(q).reshape(K // 16, 16, 3).transpose(1, 0, 2)
+    assert np.array_equal(act, wts)
+
+
+def test_pack_act_a6_one_code_touches_one_unit():
+    M, K = 3, 256
+    base = oracle.pack_act_a6(np.zeros((M, K), np.int8)).reshape(-1)
+    assert not base.any()
+    for m, k, code in [(0, 0, 1), (1, 17, -32), (2, 255, 31), (2, 128, -1)]:
+        qa = np.zeros((M, K), np.int8)
+        qa[m, k] = code
+        d = oracle.pack_act_a6(qa).reshape(-1)
+        changed = sorted({int(i) // 3 for i in np.flatnonzero(d)})
+        assert changed == [m * (K // 16) + k // 16]
+
+
+def test_pack_act_a6_round_trip_and_range():
+    rng = np.random.default_rng(12)
+    qa = rng.integers(-32, 32, (5, 1152)).astype(np.int8)
+    assert np.array_equal(oracle.unpack_act_a6(oracle.pack_act_a6(qa), 1152), qa)
+    # the A6 quantizer's codes (|q| <= 31) always fit; A8 codes beyond 6 bits do not
+    x = synth.activations(synth.derive_seed(synth.BASE_SEED, "a6pin"), 4, 512)
+    qa6, _ = oracle.quant_act(x, 6)
+    assert np.array_equal(oracle.unpack_act_a6(oracle.pack_act_a6(qa6), 512), qa6)
+    for bad in (32, -33, 127, -127):
+        q = np.zeros((1, 16), np.int8)
+        q[0, 3] = bad
+        try:
+            oracle.pack_act_a6(q)
+        except ValueError:
+            continue
+        raise AssertionError(f"code {bad} does not fit 6 bits but was packed")
+
+
+# ---------------------------------------------------------------------------
 # quantizers
 # ---------------------------------------------------------------------------
 
