@@ -95,6 +95,10 @@ def parse():
                    help="print a markdown summary of a rocprofv3 --kernel-trace database of a "
                         "bench run (per-kernel times, GEMM launches by grid, the prefill "
                         "kernel's int8 fraction recomputed from the trace) and exit")
+    p.add_argument("--a6-packed", action="store_true",
+                   help="also compare, at every M <= 64 and layer, the streaming GEMM over one "
+                        "byte per A6 code with flexq_gemm_w6a6_packed over 6-bit codes, and the "
+                        "two activation quantizers (key a6_packed)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="first run one device-to-device copy of this many MiB (the known-size "
                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -582,7 +586,64 @@ def main():
                                                   if kernel_of[k] == "splitk"),
                          "tops": round(split_all["tops"], 1), "gbs": round(split_all["gbs"], 1),
                          "ms_per_step": round(split_all["ms"], 4)}
+    if args.a6_packed:
+        tail = {k: out.pop(k) for k in ("peaks", "roofline_decode", "targets", "splitk")
+                if k in out}
+        out["a6_packed"] = a6_packed_ab(fq, torch, dev, bufs, packed, m_list, REPS)
+        out.update(tail)
     print(json.dumps(out, separators=(",", ":")), flush=True)
+
+
+def a6_packed_ab(fq, torch, dev, bufs, packed, m_list, reps):
+    """6-bit activation storage against one byte per code, at every M <= 64 and layer
+    (A6): the streaming GEMM (flexq_gemm_w6ax on FLEXQ_PATH_DECODE against
+    flexq_gemm_w6a6_packed) on rotating weight copies, and the activation quantizer
+    (flexq_quant_act against flexq_quant_act_a6_packed).  Each is the best of 4 runs of
+    `reps` back-to-back launches, the two variants alternating, a busy kernel first;
+    `same_bits` says whether the two GEMMs gave the same Y."""
+    sink = torch.empty(fq.peak_sink_bytes(), dtype=torch.uint8, device=dev)
+    clock = torch.zeros(2, dtype=torch.int64, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(runs):
+        t = {}
+        for rnd in range(4):
+            for name in (list(runs) if rnd % 2 == 0 else list(runs)[::-1]):
+                fq.peak_mfma_i8(400, 0, sink, clock)
+                e0.record()
+                for i in range(reps):
+                    runs[name](i)
+                e1.record()
+                torch.cuda.synchronize()
+                t[name] = min(t.get(name, float("inf")), e0.elapsed_time(e1) / reps * 1e3)
+        return t
+
+    gemm_rows, quant_rows = [], []
+    for M in sorted(m for m in m_list if m <= 64):
+        for name, (N, K) in LAYERS.items():
+            xd = bufs[(M, name)][1]
+            qa = torch.empty((M, K), dtype=torch.int8, device=dev)
+            qp = torch.empty((M, 3 * K // 16), dtype=torch.int32, device=dev)
+            sa = torch.empty((K // GROUP, M), dtype=torch.float32, device=dev)
+            sap = torch.empty_like(sa)
+            yb = torch.empty((M, N), dtype=torch.float16, device=dev)
+            yp = torch.empty_like(yb)
+            q = best({"bytes": lambda i: fq.quant_act(xd, 6, q_a=qa, s_a=sa),
+                      "packed": lambda i: fq.quant_act_a6_packed(xd, q_a6p=qp, s_a=sap)})
+            cps = packed[name]
+            g = best({
+                "bytes": lambda i: fq.gemm_w6ax(qa, sa, *cps[i % len(cps)], N, 6, y=yb,
+                                                path=fq.PATH_DECODE),
+                "packed": lambda i: fq.gemm_w6a6_packed(qp, sap, *cps[i % len(cps)], N, y=yp)})
+            same = bool(torch.equal(yb.view(torch.int16), yp.view(torch.int16)) and
+                        torch.equal(sa.view(torch.int32), sap.view(torch.int32)))
+            gemm_rows.append([name, M, round(g["bytes"], 2), round(g["packed"], 2),
+                              round(g["bytes"] / g["packed"], 3), same])
+            quant_rows.append([name, M, round(q["bytes"], 2), round(q["packed"], 2),
+                               round(q["bytes"] / q["packed"], 3)])
+    cols = ["layer", "M", "us_bytes", "us_packed", "speedup"]
+    return {"gemm_cols": cols + ["same_bits"], "gemm": gemm_rows, "quant_cols": cols,
+            "quant": quant_rows}
 
 
 def measure_peaks(fq, torch, dev, layers):

@@ -37,6 +37,10 @@
  *       The unit of rows n, codes k = 16u .. 16u+15 starts at dword
  *         3 * (((n / 16) * (K / 16) + u) * 16 + n % 16),
  *       i.e. 16-row tiles, unit index major, row-in-tile minor.
+ *   q_a6p                   A6 codes packed (flexq_quant_act_a6_packed): the w_packed
+ *       unit encoding above, 16 codes per 3 dwords; the unit of row m, codes
+ *       k = 16u .. 16u+15 starts at dword 3 * (m * (K / 16) + u), i.e. the units of
+ *       a token row one after another, 0.75 * K bytes per row.
  *   Y   fp16 [M][N]
  *
  * Quantizers (symmetric, round half to even, IEEE binary32 division):
@@ -126,6 +130,35 @@ flexq_status flexq_pack_w6(const uint16_t* w_fp16, int64_t N, int64_t K, int32_t
    M == 0 is a no-op.  Errors as for flexq_pack_w6, plus INVALID_VALUE for abits. */
 flexq_status flexq_quant_act(const uint16_t* x_fp16, int64_t M, int64_t K, int32_t group_size,
                              int32_t abits, int8_t* q_a, float* s_a, void* stream);
+
+/* Bytes of q_a6p for an M x K activation: 0.75 * M * K (12 bytes per 16 codes).
+   Returns 0 for M <= 0, K <= 0 or K not a multiple of 16. */
+size_t flexq_packed_a6_bytes(int64_t M, int64_t K);
+
+/* flexq_quant_act with abits = 6, the codes stored at 6 bits (FlexQ abstract: W6A6
+   holds activations at 6 bits; layout q_a6p in the preamble): the same codes and
+   the same s_a bits as flexq_quant_act(..., abits = 6, ...), at 0.75 bytes per code.
+     x_fp16 [M][K] fp16 bits, 16-byte aligned                      (input)
+     q_a6p  flexq_packed_a6_bytes(M, K) bytes, 16-byte aligned      (output)
+     s_a    [K/128][M] fp32, 4-byte aligned                          (output)
+   M == 0 is a no-op.  Errors as for flexq_quant_act (without abits). */
+flexq_status flexq_quant_act_a6_packed(const uint16_t* x_fp16, int64_t M, int64_t K,
+                                       int32_t group_size, uint32_t* q_a6p, float* s_a,
+                                       void* stream);
+
+/* The W6A6 GEMM over packed A6 activations (q_a6p from flexq_quant_act_a6_packed):
+   the weight-streaming kernel of FLEXQ_PATH_DECODE, which unpacks each activation
+   unit as it unpacks the weights.  Y is bit-identical to flexq_gemm_w6ax on the
+   unpacked codes (abits = 6).  Any M is accepted; it is meant for few tokens
+   (M <= FLEXQ_DECODE_MAX_M), since above that the weights are streamed once per 64
+   rows.
+     q_a6p  packed codes, 16-byte aligned     s_a, w_packed, s_w_fp16, y_fp16 as for
+                                              flexq_gemm_w6ax
+   M == 0 or N == 0 is a no-op.  Errors as for flexq_gemm_w6ax (without abits). */
+flexq_status flexq_gemm_w6a6_packed(const uint32_t* q_a6p, const float* s_a,
+                                    const uint32_t* w_packed, const uint16_t* s_w_fp16,
+                                    int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                    uint16_t* y_fp16, void* stream);
 
 /* Y = sum over groups of int32 group dot x s_w x s_a, fp32 accumulation, fp16 out
    (blog, "Bridging Software and Hardware with BTC": exact integer group products,

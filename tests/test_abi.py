@@ -110,6 +110,46 @@ def test_quant_act_rejects_bad_arguments(flexq):
     assert f(A16, 1 << 21, 128, 128, 6, 2 * A16, 3 * A16, None) == UNSUPPORTED  # M limit
 
 
+def test_a6_packed_entry_points_reject_bad_arguments(flexq):
+    assert flexq.flexq_packed_a6_bytes(4, 4096) == 4 * 4096 * 3 // 4
+    assert flexq.flexq_packed_a6_bytes(1, 8) == 0
+    assert flexq.flexq_packed_a6_bytes(0, 128) == 0
+    q = flexq.flexq_quant_act_a6_packed
+    assert q(None, 4, 128, 128, 2 * A16, 3 * A16, None) == INVALID
+    assert q(A16, 4, 128, 128, None, 3 * A16, None) == INVALID
+    assert q(A16, 4, 128, 128, 2 * A16, None, None) == INVALID
+    assert q(A16, -1, 128, 128, 2 * A16, 3 * A16, None) == INVALID
+    assert q(A16, 4, 100, 128, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert q(A16, 4, 128, 64, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert q(A16 + 2, 4, 128, 128, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert q(A16, 4, 128, 128, 2 * A16 + 4, 3 * A16, None) == UNSUPPORTED
+    assert q(A16, 4, 128, 128, 2 * A16, 3 * A16 + 2, None) == UNSUPPORTED
+    assert q(A16, 4, 128, 128, A16 + 512, 3 * A16, None) == INVALID   # codes inside x
+    assert q(A16, 4, 128, 128, 2 * A16, 2 * A16 + 368, None) == INVALID  # s_a inside codes
+    assert q(None, 0, 128, 128, None, None, None) == SUCCESS
+    g = flexq.flexq_gemm_w6a6_packed
+    args = dict(qp=A16, sa=2 * A16, wp=3 * A16, sw=4 * A16, y=5 * A16)
+
+    def call(M=4, N=16, K=128, group=128, **kw):
+        a = {**args, **kw}
+        return g(a["qp"], a["sa"], a["wp"], a["sw"], M, N, K, group, a["y"], None)
+
+    for k in args:
+        assert call(**{k: None}) == INVALID, k
+    assert call(M=-1) == INVALID
+    assert call(N=-16) == INVALID
+    assert call(K=0) == INVALID
+    assert call(K=130) == UNSUPPORTED
+    assert call(N=24) == UNSUPPORTED
+    assert call(group=256) == UNSUPPORTED
+    assert call(qp=A16 + 4) == UNSUPPORTED
+    assert call(wp=3 * A16 + 4) == UNSUPPORTED
+    assert call(y=5 * A16 + 2) == UNSUPPORTED
+    assert call(y=A16 + 256) == INVALID       # Y overlaps the packed codes (4 x 96 bytes)
+    assert call(M=0, qp=None, y=None) == SUCCESS
+    assert call(N=0, wp=None, y=None) == SUCCESS
+
+
 def test_gemm_rejects_bad_arguments(flexq):
     f = flexq.flexq_gemm_w6ax
     g = flexq.flexq_gemm_w6ax_path
@@ -309,6 +349,27 @@ def test_binding_checks_the_other_entry_points():
                                 dots=torch.zeros(2, 32, 1, dtype=i32))
     with pytest.raises(TypeError, match="CUDA"):
         fq.gemm_w6ax_group_dots(torch.zeros(2, 256, dtype=i8), wp, 32)
+    # packed A6 activations: int32 [M][3K/16]
+    with pytest.raises(ValueError, match="q_a6p must have shape"):
+        fq.quant_act_a6_packed(x, q_a6p=torch.zeros(2, 32, dtype=i32))
+    with pytest.raises(TypeError, match="q_a6p must be"):
+        fq.quant_act_a6_packed(x, q_a6p=torch.zeros(2, 48, dtype=i8))
+    with pytest.raises(TypeError, match="CUDA"):
+        fq.quant_act_a6_packed(x)
+    qp = torch.zeros(2, 48, dtype=i32)
+    sa = torch.zeros(2, 2, dtype=f32)
+    with pytest.raises(ValueError, match="multiple of 3"):
+        fq.gemm_w6a6_packed(torch.zeros(2, 47, dtype=i32), sa, wp, sw, 32)
+    with pytest.raises(ValueError, match="multiple of 128"):
+        fq.gemm_w6a6_packed(torch.zeros(2, 45, dtype=i32), sa, wp, sw, 32)
+    with pytest.raises(ValueError, match="s_a must have shape"):
+        fq.gemm_w6a6_packed(qp, torch.zeros(2, 1, dtype=f32), wp, sw, 32)
+    with pytest.raises(ValueError, match="w_packed holds"):
+        fq.gemm_w6a6_packed(qp, sa, torch.zeros(10, dtype=i32), sw, 32)
+    with pytest.raises(ValueError, match="y must have shape"):
+        fq.gemm_w6a6_packed(qp, sa, wp, sw, 32, y=torch.zeros(2, 16, dtype=f16))
+    with pytest.raises(TypeError, match="CUDA"):
+        fq.gemm_w6a6_packed(qp, sa, wp, sw, 32)
 
 
 def test_auto_path_rule(flexq):

@@ -18,7 +18,9 @@ order of the definition.  Where the split-K plan cuts K into slices (mid-sized M
 narrow layers), flexq_gemm_w6ax_splitk runs in the planned configuration too and its
 whole Y and fp32 accumulator are checked against the tolerance for a changed
 summation order (tests/tolerance.py).  At M <= 64 the one-call layer (flexq_linear_w6ax) must
-also give the two-call result in full.
+also give the two-call result in full, and for A6 the packed activations
+(flexq_quant_act_a6_packed) and the streaming GEMM over them (flexq_gemm_w6a6_packed)
+are checked whole against the oracle's packing and Y.
 
 Workloads: the toy W6A6 layer, LLaMA-2-7B W6A6 (M 1/16/128), LLaMA-2-13B W6A8
 (M 1/64/512), LLaMA-2-70B in W6A6 and W6A8 (M 1/16/64/256/1024/4096), the distinct
@@ -188,6 +190,22 @@ def test_full_size(fq, wname, lname):
                 if M <= FULL_Y_MAX_M:
                     y_lin = fq.linear_w6ax(xd, wp, sw, N, abits)
                     assert torch.equal(y_lin.view(torch.int16), y.view(torch.int16))
+                if M <= FULL_Y_MAX_M and abits == 6:
+                    # 6-bit activation storage: the whole packed tensor, and the whole Y
+                    # of the streaming kernel over it
+                    say(f"{wname} {lname}: M={M}: packed A6 activations")
+                    qp, sap = fq.quant_act_a6_packed(xd)
+                    yp = fq.gemm_w6a6_packed(qp, sap, wp, sw, N)
+                    torch.cuda.synchronize()
+                    qp_ref = oracle.pack_act_a6(qa_ref)
+                    qp_got = qp.cpu().numpy().view(np.uint32)
+                    assert np.array_equal(qp_got, qp_ref), first_diffs(
+                        qp_got, qp_ref, lambda b: (int(b[0]), int(b[1]) // 3))
+                    assert torch.equal(sap.view(torch.int32), sa.view(torch.int32))
+                    yp_got = yp.cpu().numpy().view(np.uint16)
+                    assert np.array_equal(yp_got, y_ref.view(np.uint16)), first_diffs(
+                        yp_got, y_ref.view(np.uint16), lambda b: (int(b[0]), int(b[1])))
+                    del qp, sap, yp
             else:
                 rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 2)]))
                 y_ref = oracle.gemm(np.ascontiguousarray(qa_ref[rows]),

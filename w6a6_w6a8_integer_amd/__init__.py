@@ -48,6 +48,9 @@ SIGNATURES = {
     "flexq_packed_w6_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "flexq_pack_w6": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "flexq_quant_act": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _P, _P]),
+    "flexq_packed_a6_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "flexq_quant_act_a6_packed": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "flexq_gemm_w6a6_packed": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P]),
     "flexq_gemm_w6ax": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P]),
     "flexq_gemm_w6ax_path": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32,
                                             _P, _P]),
@@ -216,6 +219,55 @@ def quant_act(x: torch.Tensor, abits: int, q_a: torch.Tensor | None = None,
     _check(lib().flexq_quant_act(x.data_ptr(), M, K, GROUP, abits, q_a.data_ptr(),
                                  s_a.data_ptr(), _stream(x)), "flexq_quant_act")
     return q_a, s_a
+
+
+def packed_a6_bytes(M: int, K: int) -> int:
+    return int(lib().flexq_packed_a6_bytes(M, K))
+
+
+def quant_act_a6_packed(x: torch.Tensor, q_a6p: torch.Tensor | None = None,
+                        s_a: torch.Tensor | None = None):
+    """fp16 X[M][K] -> (q_a6p int32[M][3*K/16]: the A6 codes packed 16 per 3 dwords,
+    s_a fp32[K/128][M]); the codes and scales of quant_act(x, 6)."""
+    _matrix(x, torch.float16, "x")
+    M, K = x.shape
+    G = _groups(K, "quant_act_a6_packed")
+    if q_a6p is None:
+        q_a6p = torch.empty((M, 3 * K // 16), dtype=torch.int32, device=x.device)
+    if s_a is None:
+        s_a = torch.empty((G, M), dtype=torch.float32, device=x.device)
+    _tensor(q_a6p, torch.int32, "q_a6p", shape=(M, 3 * K // 16))
+    _tensor(s_a, torch.float32, "s_a", shape=(G, M))
+    _on_gpu(x=x, q_a6p=q_a6p, s_a=s_a)
+    _check(lib().flexq_quant_act_a6_packed(x.data_ptr(), M, K, GROUP, q_a6p.data_ptr(),
+                                           s_a.data_ptr(), _stream(x)),
+           "flexq_quant_act_a6_packed")
+    return q_a6p, s_a
+
+
+def gemm_w6a6_packed(q_a6p: torch.Tensor, s_a: torch.Tensor, w_packed: torch.Tensor,
+                     s_w: torch.Tensor, N: int, y: torch.Tensor | None = None):
+    """Y fp16[M][N] from packed A6 activations (q_a6p int32[M][3*K/16], s_a
+    fp32[K/128][M]) and packed weights: the weight-streaming kernel, the bits of
+    gemm_w6ax on the unpacked codes."""
+    _matrix(q_a6p, torch.int32, "q_a6p")
+    M, words = q_a6p.shape
+    if words % 3:
+        raise ValueError(f"q_a6p has {words} dwords per row; a multiple of 3 is needed")
+    K = words // 3 * 16
+    G = _groups(K, "gemm_w6a6_packed")
+    N = _cols(N)
+    _tensor(s_a, torch.float32, "s_a", shape=(G, M))
+    _packed(w_packed, N, K)
+    _tensor(s_w, torch.float16, "s_w", shape=(G, N))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=q_a6p.device)
+    _tensor(y, torch.float16, "y", shape=(M, N))
+    _on_gpu(q_a6p=q_a6p, s_a=s_a, w_packed=w_packed, s_w=s_w, y=y)
+    _check(lib().flexq_gemm_w6a6_packed(q_a6p.data_ptr(), s_a.data_ptr(), w_packed.data_ptr(),
+                                        s_w.data_ptr(), M, N, K, GROUP, y.data_ptr(),
+                                        _stream(q_a6p)), "flexq_gemm_w6a6_packed")
+    return y
 
 
 def gemm_w6ax(q_a: torch.Tensor, s_a: torch.Tensor, w_packed: torch.Tensor, s_w: torch.Tensor,

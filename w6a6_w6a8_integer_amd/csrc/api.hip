@@ -225,6 +225,54 @@ flexq_status flexq_quant_act(const uint16_t* x_fp16, int64_t M, int64_t K, int32
                                           (hipStream_t)stream));
 }
 
+size_t flexq_packed_a6_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % 16 != 0) return 0;
+  return (size_t)M * (size_t)K / 16 * 12;
+}
+
+flexq_status flexq_quant_act_a6_packed(const uint16_t* x_fp16, int64_t M, int64_t K,
+                                       int32_t group_size, uint32_t* q_a6p, float* s_a,
+                                       void* stream) {
+  FLEXQ_TRY(check_m(M));
+  FLEXQ_TRY(check_k(K, group_size));
+  FLEXQ_TRY(check_scales(M, K));
+  if (M == 0) return FLEXQ_SUCCESS;
+  if (!x_fp16 || !q_a6p || !s_a) return FLEXQ_ERROR_INVALID_VALUE;
+  if (!aligned(x_fp16, 16) || !aligned(q_a6p, 16) || !aligned(s_a, 4))
+    return FLEXQ_ERROR_UNSUPPORTED;
+  const Range in = range_of(x_fp16, (uint64_t)M * K * 2);
+  const Range oq = range_of(q_a6p, flexq_packed_a6_bytes(M, K));
+  const Range os = range_of(s_a, (uint64_t)M * (K / kGroup) * 4);
+  if (overlap(in, oq) || overlap(in, os) || overlap(oq, os)) return FLEXQ_ERROR_INVALID_VALUE;
+  return launched(
+      flexq::launch_quant_act_a6_packed(x_fp16, M, K, q_a6p, s_a, (hipStream_t)stream));
+}
+
+flexq_status flexq_gemm_w6a6_packed(const uint32_t* q_a6p, const float* s_a,
+                                    const uint32_t* w_packed, const uint16_t* s_w_fp16,
+                                    int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                    uint16_t* y_fp16, void* stream) {
+  FLEXQ_TRY(check_m(M));
+  FLEXQ_TRY(check_n(N));
+  FLEXQ_TRY(check_k(K, group_size));
+  FLEXQ_TRY(check_scales(M, K));
+  FLEXQ_TRY(check_scales(N, K));
+  if (M == 0 || N == 0) return FLEXQ_SUCCESS;
+  if (!q_a6p || !s_a || !w_packed || !s_w_fp16 || !y_fp16) return FLEXQ_ERROR_INVALID_VALUE;
+  if (!aligned(q_a6p, 16) || !aligned(w_packed, 16) || !aligned(s_a, 4) ||
+      !aligned(s_w_fp16, 2) || !aligned(y_fp16, 4))
+    return FLEXQ_ERROR_UNSUPPORTED;
+  const uint64_t G = (uint64_t)(K / kGroup);
+  const Range o = range_of(y_fp16, (uint64_t)M * N * 2);
+  if (overlap(o, range_of(q_a6p, flexq_packed_a6_bytes(M, K))) ||
+      overlap(o, range_of(s_a, (uint64_t)M * G * 4)) ||
+      overlap(o, range_of(w_packed, (uint64_t)N * K * 3 / 4)) ||
+      overlap(o, range_of(s_w_fp16, (uint64_t)N * G * 2)))
+    return FLEXQ_ERROR_INVALID_VALUE;
+  return launched(flexq::launch_gemm_decode_a6p(q_a6p, s_a, w_packed, s_w_fp16, M, N, K, y_fp16,
+                                                (hipStream_t)stream));
+}
+
 flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a, const uint32_t* w_packed,
                                   const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K,
                                   int32_t group_size, int32_t abits, int32_t path,

@@ -22,6 +22,7 @@
 // ascending group order, so the result equals the sequential definition bit for
 // bit.  The last round of an item stores its fp16 outputs.
 #include <atomic>
+#include <type_traits>
 
 #include "kernels.h"
 #include "w6_device.h"
@@ -38,12 +39,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                            kRsrcWord3);
 }
 
-template <int MT, int T>
+// Activation fragment as loaded: 16 int8 codes, or (PA) one packed 6-bit unit.
+template <bool PA>
+using AFrag = typename std::conditional<PA, u32x3, i32x4>::type;
+
+template <int MT, int T, bool PA>
 struct Bundle {
-  u32x3 w[T][2];    // per 16-column tile: two weight units (k-blocks of 64)
-  i32x4 a[MT][2];   // activation fragments, rows ms*16 + lane%16
-  float sa;         // s_a[row = lane][g]
-  uint32_t sw;      // s_w[col = lane % (16*T)][g] (fp16 bits)
+  u32x3 w[T][2];        // per 16-column tile: two weight units (k-blocks of 64)
+  AFrag<PA> a[MT][2];   // activation fragments, rows ms*16 + lane%16
+  float sa;             // s_a[row = lane][g]
+  uint32_t sw;          // s_w[col = lane % (16*T)][g] (fp16 bits)
 };
 
 // Position of a step in a workgroup's stream.  The workgroup's items are cut into
@@ -82,12 +87,17 @@ struct Cursor {
 // workgroup quantizes fp16 X (x, qmax) once into LDS -- the same per-group rule and
 // helper as flexq_quant_act, so codes and scales are bit-identical -- and the
 // activation fragments and scales are read from there instead of q_a / s_a.
-template <int MT, int T, int S, int P, int C, bool FQ>
+// PA: qa holds A6 codes packed 16 per 3 dwords, the units of a row in order
+// (0.75 K bytes per row); each fragment is one 12-byte unit, unpacked like the
+// weights into bytes 4 * q_a, so the MFMA dots are 16 d and the fold scales by
+// s_w / 16 instead of s_w / 4 (both exact).
+template <int MT, int T, int S, int P, int C, bool FQ, bool PA>
 __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint32_t* __restrict__ wp,
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ y, int ntiles16,
     int ntiles, int items, int per_wg, const uint16_t* __restrict__ x, int qmax) {
   static_assert(!FQ || MT == 1, "the fused quantizer covers one pass of up to 16 rows");
+  static_assert(!(FQ && PA), "the fused quantizer keeps its codes in LDS");
   static_assert(P % 2 == 0, "slot parity must be static");
   constexpr int U = C > P ? C : P;  // steps per loop iteration: ring slot and item static
   static_assert(U % P == 0 && U % C == 0, "step unroll");
@@ -122,17 +132,20 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
   const int8_t* lq = lds_x;
   const float* lsc = reinterpret_cast<const float*>(lds_x + (fq_rows * K + 15) / 16 * 16);
 
-  const uint32_t a_lane_off = (uint32_t)(lane & 15) * (uint32_t)K + (uint32_t)(lane >> 4) * 16u;
+  // bytes per activation row, and per group and 64-deep k-block of a row
+  const uint32_t a_row = PA ? (uint32_t)K / 4u * 3u : (uint32_t)K;
+  constexpr uint32_t a_grp = PA ? 96u : 128u, a_blk = PA ? 48u : 64u;
+  const uint32_t a_lane_off = (uint32_t)(lane & 15) * a_row + (uint32_t)(lane >> 4) * (a_blk / 4u);
 
   // Loads of step c.  Out-of-range buffer loads return zero: rows past the pass and
   // groups >= G vanish; empty steps read from empty buffers.  The activation
   // fragments are loaded by the chunk's first item slot only.
-  auto load = [&](Bundle<MT, T>& b, const Cursor& c, auto first_slot) {
+  auto load = [&](Bundle<MT, T, PA>& b, const Cursor& c, auto first_slot) {
     const bool live = c.live(item_end);
     const int tile = live ? c.tile0 + c.i : 0;  // in units of COLS columns
     const int row0 = live ? c.pass * 64 : 0;
     const int rows = live ? min(ROWS, M - row0) : 0;
-    const auto ra = make_rsrc(qa + (size_t)row0 * K, (uint32_t)rows * (uint32_t)K);
+    const auto ra = make_rsrc(qa + (size_t)row0 * a_row, (uint32_t)rows * a_row);
     // scales are group-major (s_a[g][m] at g*M + m, s_w[g][n] at g*N + n); entries of
     // rows past the pass or columns past N are read but never used
     const auto rsa = make_rsrc(sa + row0, live ? (uint32_t)((size_t)G * M - row0) * 4u : 0u);
@@ -153,9 +166,13 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
 #pragma unroll
       for (int ms = 0; ms < MT; ++ms) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          b.a[ms][j] = __builtin_amdgcn_raw_buffer_load_b128(
-              ra, a_lane_off + (uint32_t)(ms * 16) * (uint32_t)K + g * 128u + j * 64u, 0, 0);
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t off = a_lane_off + (uint32_t)(ms * 16) * a_row + g * a_grp + j * a_blk;
+          if constexpr (PA)
+            b.a[ms][j] = __builtin_amdgcn_raw_buffer_load_b96(ra, off, 0, 0);
+          else
+            b.a[ms][j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+        }
       }
     }
     // (every offset goes in the VGPR operand: the range check that zeroes reads
@@ -170,7 +187,7 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
   Cursor start{item_begin, 0, item_begin % ntiles, item_begin / ntiles, 0, 0};
   start.start_chunk(C, item_end, ntiles);
   Cursor cl = start;  // next step to load; step k goes to ring slot k % P
-  Bundle<MT, T> ring[P];
+  Bundle<MT, T, PA> ring[P];
   unroll([&](auto pc) {
     constexpr int p = decltype(pc)::value;
     load(ring[p], cl, std::integral_constant<bool, p % C == 0>{});
@@ -213,7 +230,7 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
       constexpr int p = decltype(pc)::value;
       constexpr int slot = p & 1;
       constexpr int ci = p % C;  // item slot of this step
-      Bundle<MT, T>& b = ring[p % P];
+      Bundle<MT, T, PA>& b = ring[p % P];
       // FQ: this step's group in the LDS copy (clamped: rounds past the last group
       // are never folded), and a row that exists (rows past M are never stored)
       const int fq_g = FQ ? min(cp.r * S + wave, G - 1) : 0;
@@ -227,12 +244,17 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
         } else {
 #pragma unroll
           for (int ms = 0; ms < MT; ++ms) {
-            a_cur[ms][0] = b.a[ms][0];
-            a_cur[ms][1] = b.a[ms][1];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              if constexpr (PA)
+                a_cur[ms][j] = unpack_unit_x4(b.a[ms][j][0], b.a[ms][j][1], b.a[ms][j][2]);
+              else
+                a_cur[ms][j] = b.a[ms][j];
+            }
           }
         }
       }
-      // exact integer group products (4*d, see w6_device.h)
+      // exact integer group products (4*d, see w6_device.h; PA: 16*d)
       i32x4 d[T][MT];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
@@ -245,7 +267,8 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
         }
       }
       // park dots 4d (row-major [row][col]) and this group's scales, s_w as s_w / 4
-      // (exact), so the fold forms t = RN(d * s_w) as float(4d) * (s_w / 4)
+      // (exact), so the fold forms t = RN(d * s_w) as float(4d) * (s_w / 4); with PA
+      // as float(16d) * (s_w / 16), |16d| <= 16 * 128 * 31 * 32 < 2^24 being exact too
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -266,7 +289,8 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
       } else {
         if (lane < ROWS) lds_sa[slot][wave][lane] = b.sa;
       }
-      if (lane < COLS) lds_sw[slot][wave][lane] = 0.25f * half_bits_to_float((uint16_t)b.sw);
+      if (lane < COLS)
+        lds_sw[slot][wave][lane] = (PA ? 0.0625f : 0.25f) * half_bits_to_float((uint16_t)b.sw);
       // the step P ahead lands in this ring slot; it is the chunk's first item slot
       // exactly when this one is (P is a multiple of C, or C of P)
       load(b, cl, std::integral_constant<bool, ((p + P) % C) == 0>{});
@@ -298,7 +322,7 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
 #pragma unroll
                 for (int w = 0; w < S; ++w) {
                   if (w < ng) {
-                    const float t = (float)dv[w][r] * swv[w];  // float(4d) is exact
+                    const float t = (float)dv[w][r] * swv[w];  // float(4d) exact
                     a = fmaf(t, sav[w][r], a);
                   }
                 }
@@ -406,19 +430,19 @@ int auto_gemm_path(int64_t M, int64_t N) {
   return M >= 48 && prefill_tile(M, N) == kTile64x128 ? 2 : 1;
 }
 
-template <int MT, int T, int S, int P, int C, bool FQ = false>
+template <int MT, int T, int S, int P, int C, bool FQ = false, bool PA = false>
 static hipError_t launch_decode_c(const int8_t* qa, const float* sa, const uint32_t* wp,
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                   uint16_t* y, int64_t ntiles16, int64_t ntiles, int64_t items,
                                   int64_t per_wg, int64_t grid, hipStream_t stream,
                                   const uint16_t* x = nullptr, int qmax = 0) {
   const size_t lds_x = FQ ? fused_quant_lds_bytes(M, K) : 0;
-  return launch_kernel_lds(gemm_decode_kernel<MT, T, S, P, C, FQ>, dim3((unsigned)grid),
+  return launch_kernel_lds(gemm_decode_kernel<MT, T, S, P, C, FQ, PA>, dim3((unsigned)grid),
                            dim3(64 * S), lds_x, stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, y,
                            (int)ntiles16, (int)ntiles, (int)items, (int)per_wg, x, qmax);
 }
 
-template <int MT, int T, int S, int P, int CMAX, bool FQ = false>
+template <int MT, int T, int S, int P, int CMAX, bool FQ = false, bool PA = false>
 static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint32_t* wp,
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                   uint16_t* y, hipStream_t stream, bool chunk_few_rows = false,
@@ -435,24 +459,26 @@ static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint3
   // few token rows not worth the empty steps of a partial chunk, except where the
   // caller found it pays)
   if (M <= 4 && !chunk_few_rows)
-    return launch_decode_c<MT, T, S, P, 1, FQ>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles,
-                                               items, per_wg, grid, stream, x, qmax);
+    return launch_decode_c<MT, T, S, P, 1, FQ, PA>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles,
+                                                   items, per_wg, grid, stream, x, qmax);
   if (CMAX >= 8 && per_wg >= 5)
-    return launch_decode_c<MT, T, S, P, (CMAX >= 8 ? 8 : 1), FQ>(
+    return launch_decode_c<MT, T, S, P, (CMAX >= 8 ? 8 : 1), FQ, PA>(
         qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items, per_wg, grid, stream, x, qmax);
   if (CMAX >= 4 && per_wg >= 3)
-    return launch_decode_c<MT, T, S, P, (CMAX >= 4 ? 4 : 1), FQ>(
+    return launch_decode_c<MT, T, S, P, (CMAX >= 4 ? 4 : 1), FQ, PA>(
         qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items, per_wg, grid, stream, x, qmax);
   if (CMAX >= 2 && per_wg >= 2)
-    return launch_decode_c<MT, T, S, P, (CMAX >= 2 ? 2 : 1), FQ>(
+    return launch_decode_c<MT, T, S, P, (CMAX >= 2 ? 2 : 1), FQ, PA>(
         qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items, per_wg, grid, stream, x, qmax);
-  return launch_decode_c<MT, T, S, P, 1, FQ>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles,
-                                             items, per_wg, grid, stream, x, qmax);
+  return launch_decode_c<MT, T, S, P, 1, FQ, PA>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles,
+                                                 items, per_wg, grid, stream, x, qmax);
 }
 
-hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t* wp,
-                              const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
-                              hipStream_t stream) {
+// The kernel configuration for an M x N x K product (PA: packed A6 activations).
+template <bool PA>
+static hipError_t launch_decode_any(const int8_t* qa, const float* sa, const uint32_t* wp,
+                                    const uint16_t* sw, int64_t M, int64_t N, int64_t K,
+                                    uint16_t* y, hipStream_t stream) {
   // rows per pass: 16 * MT; more passes over W only when M > 64
   const int64_t rows = M > 64 ? 64 : M;
   const int64_t cu = device_cu_count();
@@ -466,16 +492,19 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
     // paired tiles, o 12.3 -> 11.3 us with chunks of single tiles).
     if (N / 16 <= 3 * cu && K <= 16384) {
       if (rows <= 4 && N / 16 > 2 * cu)
-        return launch_decode_t<1, 2, 16, 2, 2>(qa, sa, wp, sw, M, N, K, y, stream, true);
+        return launch_decode_t<1, 2, 16, 2, 2, false, PA>(qa, sa, wp, sw, M, N, K, y, stream,
+                                                          true);
       if (rows <= 4)
-        return launch_decode_t<1, 1, 16, 2, 2>(qa, sa, wp, sw, M, N, K, y, stream, true);
-      return launch_decode_t<1, 1, 16, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
+        return launch_decode_t<1, 1, 16, 2, 2, false, PA>(qa, sa, wp, sw, M, N, K, y, stream,
+                                                          true);
+      return launch_decode_t<1, 1, 16, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
     }
     // Paired tiles: 16 waves for up to 4 rows; from 5 rows 8 waves with the
     // column-segment fold (70B down at M = 16: 39 -> 36 us; 16 waves stay faster
     // at M = 1, where the fold is tiny and more waves keep more loads in flight).
-    if (rows <= 4) return launch_decode_t<1, 2, 16, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
-    return launch_decode_t<1, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
+    if (rows <= 4)
+      return launch_decode_t<1, 2, 16, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
+    return launch_decode_t<1, 2, 8, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
   }
   if (rows <= 32) {
     // single tiles on narrow, short layers as above; then chunks of up to 4 items.
@@ -483,11 +512,25 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
     // (activation fragments shared 8 ways; 16 waves fit only 2) and the column-
     // segment fold (70B gate_up at M = 24 / 32: 80 -> 67 / 90 -> 73 us).
     if (N / 16 <= 3 * cu && K <= 16384)
-      return launch_decode_t<2, 1, 16, 2, 4>(qa, sa, wp, sw, M, N, K, y, stream);
-    return launch_decode_t<2, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
+      return launch_decode_t<2, 1, 16, 2, 4, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
+    return launch_decode_t<2, 2, 8, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
   }
-  if (rows <= 48) return launch_decode_t<3, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
-  return launch_decode_t<4, 2, 8, 2, 8>(qa, sa, wp, sw, M, N, K, y, stream);
+  if (rows <= 48)
+    return launch_decode_t<3, 2, 8, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
+  return launch_decode_t<4, 2, 8, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
+}
+
+hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t* wp,
+                              const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                              hipStream_t stream) {
+  return launch_decode_any<false>(qa, sa, wp, sw, M, N, K, y, stream);
+}
+
+hipError_t launch_gemm_decode_a6p(const uint32_t* qp, const float* sa, const uint32_t* wp,
+                                  const uint16_t* sw, int64_t M, int64_t N, int64_t K,
+                                  uint16_t* y, hipStream_t stream) {
+  return launch_decode_any<true>(reinterpret_cast<const int8_t*>(qp), sa, wp, sw, M, N, K, y,
+                                 stream);
 }
 
 hipError_t launch_linear_decode_fused(const uint16_t* x, int64_t M, int64_t K, int qmax,

@@ -35,6 +35,16 @@ hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t*
                               const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                               hipStream_t stream);
 
+// 6-bit activation storage: A6 codes packed 16 per 3 dwords in the weight unit
+// encoding, unit (m, u = k/16) at dword 3 * (m * K/16 + u).  The quantizer gives the
+// codes and scales of launch_quant_act with qmax = 31; the streaming GEMM over them
+// gives the bits of launch_gemm_decode on the unpacked codes.
+hipError_t launch_quant_act_a6_packed(const uint16_t* x, int64_t M, int64_t K, uint32_t* qp,
+                                      float* sa, hipStream_t stream);
+hipError_t launch_gemm_decode_a6p(const uint32_t* qp, const float* sa, const uint32_t* wp,
+                                  const uint16_t* sw, int64_t M, int64_t N, int64_t K,
+                                  uint16_t* y, hipStream_t stream);
+
 // launch_kernel with `lds_bytes` of dynamic LDS.
 template <typename... Params, typename... Args>
 hipError_t launch_kernel_lds(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds_bytes,

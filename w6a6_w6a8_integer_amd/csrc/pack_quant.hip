@@ -3,6 +3,9 @@
 // Sensitivity": one scale per small group of weights or activations; FlexQ
 // abstract: 6-bit weights everywhere, 6- or 8-bit activations per layer).
 //
+// The activation quantizer can also write A6 codes packed 16 per 3 dwords (the
+// weight unit, FlexQ abstract: W6A6 holds activations at 6 bits).
+//
 // Both kernels are HBM-bound elementwise passes.  Arithmetic follows the
 // formulas of the public header exactly (IEEE division, round half to even),
 // so their outputs are bit-identical to the plain definition.
@@ -56,6 +59,9 @@ __global__ __launch_bounds__(128) void pack_w6_kernel(const uint16_t* __restrict
 
 // Thread = 8 consecutive activations; 16 adjacent lanes (one DPP row) = one
 // 128-deep group.  blockIdx.x = token row, blockIdx.y = chunk of 2048 columns.
+// PACKED (A6 only): the codes of lanes 2i and 2i+1 form one 16-code unit, which
+// the even lane writes (12 bytes at unit (m, k0 / 16) of the row-major unit grid).
+template <bool PACKED>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int M,
                                                         int K, int qmax, int8_t* __restrict__ qa,
                                                         float* __restrict__ sa) {
@@ -65,7 +71,20 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
   const u32x4 h = *reinterpret_cast<const u32x4*>(x + m * K + k0);
   float s;
   const u32x2 codes = quant8_row16(h, qmax, s);
-  *reinterpret_cast<u32x2*>(qa + m * K + k0) = codes;
+  if constexpr (PACKED) {
+    // the partner lane is in the same group, so it is active whenever this one is
+    const uint32_t p0 = (uint32_t)__shfl_xor((int)codes[0], 1);
+    const uint32_t p1 = (uint32_t)__shfl_xor((int)codes[1], 1);
+    if ((threadIdx.x & 1) == 0) {
+      const u32x3 d = pack_codes16(codes[0], codes[1], p0, p1);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(qa) + 3 * ((m * K + k0) >> 4);
+      dst[0] = d[0];
+      dst[1] = d[1];
+      dst[2] = d[2];
+    }
+  } else {
+    *reinterpret_cast<u32x2*>(qa + m * K + k0) = codes;
+  }
   if ((threadIdx.x & 15) == 0) sa[(int64_t)(k0 >> 7) * M + m] = s;  // group-major scales
 }
 
@@ -78,7 +97,15 @@ hipError_t launch_pack_w6(const uint16_t* w, int64_t N, int64_t K, uint32_t* wp,
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int qmax, int8_t* qa,
                             float* sa, hipStream_t stream) {
   dim3 grid((unsigned)M, (unsigned)((K + 2047) / 2048));
-  return launch_kernel(quant_act_kernel, grid, dim3(256), stream, x, (int)M, (int)K, qmax, qa, sa);
+  return launch_kernel(quant_act_kernel<false>, grid, dim3(256), stream, x, (int)M, (int)K, qmax,
+                       qa, sa);
+}
+
+hipError_t launch_quant_act_a6_packed(const uint16_t* x, int64_t M, int64_t K, uint32_t* qp,
+                                      float* sa, hipStream_t stream) {
+  dim3 grid((unsigned)M, (unsigned)((K + 2047) / 2048));
+  return launch_kernel(quant_act_kernel<true>, grid, dim3(256), stream, x, (int)M, (int)K, 31,
+                       reinterpret_cast<int8_t*>(qp), sa);
 }
 
 }  // namespace flexq

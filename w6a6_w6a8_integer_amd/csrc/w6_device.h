@@ -61,6 +61,20 @@ __device__ __forceinline__ u32x3 pack_unit(const int q[16]) {
   return r;
 }
 
+// The same unit from 16 int8 codes (each in [-32, 31]) held four per dword: bytes of
+// c0 = codes 0-3, c1 = 4-7, c2 = 8-11, c3 = 12-15.  The low nibble of each byte is
+// the code's 4-bit part and bits 4-5 its 2-bit part, so the planes come out with
+// masks and shifts on whole dwords.
+__device__ __forceinline__ u32x3 pack_codes16(uint32_t c0, uint32_t c1, uint32_t c2,
+                                              uint32_t c3) {
+  u32x3 r;
+  r[0] = (c0 & 0x0F0F0F0Fu) | ((c1 & 0x0F0F0F0Fu) << 4);
+  r[1] = (c2 & 0x0F0F0F0Fu) | ((c3 & 0x0F0F0F0Fu) << 4);
+  r[2] = ((c0 >> 4) & 0x03030303u) | (((c1 >> 4) & 0x03030303u) << 2) |
+         (((c2 >> 4) & 0x03030303u) << 4) | (((c3 >> 4) & 0x03030303u) << 6);
+  return r;
+}
+
 // First dword of unit (n, u = k/16) of an N x K packed weight.
 __host__ __device__ __forceinline__ int64_t unit_dword(int64_t n, int64_t u, int64_t K) {
   return 3 * (((n >> 4) * (K >> 4) + u) * 16 + (n & 15));
