@@ -162,3 +162,54 @@ def test_splitk_graph_replays_match_eager(fq):
             assert torch.equal(y.view(torch.int16), ye.view(torch.int16)), f"replay {rep} case {i}: y"
             assert torch.equal(acc.view(torch.int32), ae.view(torch.int32)), \
                 f"replay {rep} case {i}: acc"
+
+
+def test_a6_packed_graph_replays_match_eager(fq):
+    """The packed A6 quantizer and the streaming GEMM over its output, captured in one
+    HIP graph: every replay, between eager work that poisons the packed codes, the
+    scales and Y, gives the eager bits, and those equal the oracle's."""
+    cases = [(1, 512, 1024), (16, 1040, 2048), (64, 400, 1152)]
+    bufs = []
+    for i, (M, N, K) in enumerate(cases):
+        x = synth.activations(synth.derive_seed(24, "x", i), M, K)
+        w = synth.weights(synth.derive_seed(24, "w", i), N, K)
+        qa_ref, sa_ref = oracle.quant_act(x, 6)
+        wp_ref, sw_ref = oracle.pack_w6(w)
+        ref = (oracle.pack_act_a6(qa_ref), sa_ref,
+               oracle.gemm_packed(qa_ref, sa_ref, wp_ref, sw_ref, N))
+        wp, sw = fq.pack_w6(torch.from_numpy(w).to(DEV))
+        qp = torch.empty((M, 3 * K // 16), dtype=torch.int32, device=DEV)
+        sa = torch.empty((K // G, M), dtype=torch.float32, device=DEV)
+        y = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        bufs.append((N, torch.from_numpy(x).to(DEV), wp, sw, qp, sa, y, ref))
+
+    def run():
+        for (N, xd, wp, sw, qp, sa, y, _) in bufs:
+            fq.quant_act_a6_packed(xd, q_a6p=qp, s_a=sa)
+            fq.gemm_w6a6_packed(qp, sa, wp, sw, N, y=y)
+
+    run()
+    torch.cuda.synchronize()
+    for (N, xd, wp, sw, qp, sa, y, (qp_ref, sa_ref, y_ref)) in bufs:
+        assert np.array_equal(qp.cpu().numpy().view(np.uint32), qp_ref)
+        assert np.array_equal(sa.cpu().numpy().T.view(np.uint32), sa_ref.view(np.uint32))
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), y_ref.view(np.uint16))
+    eager = [(qp.clone(), sa.clone(), y.clone()) for (_, _, _, _, qp, sa, y, _) in bufs]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for (_, _, _, _, qp, sa, y, _) in bufs:
+            qp.fill_(-1)
+            sa.fill_(float("nan"))
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, ((_, _, _, _, qp, sa, y, _), (qe, se, ye)) in enumerate(zip(bufs, eager)):
+            assert torch.equal(qp, qe), f"replay {rep} case {i}: packed codes"
+            assert torch.equal(sa.view(torch.int32), se.view(torch.int32)), \
+                f"replay {rep} case {i}: scales"
+            assert torch.equal(y.view(torch.int16), ye.view(torch.int16)), f"replay {rep} case {i}: y"

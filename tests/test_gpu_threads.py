@@ -3,8 +3,9 @@ once, each thread enqueueing on a stream of its own (default priority).
 
 Four threads start together and each runs one layer 16 times, rotating through the
 one-call path (flexq_linear_w6ax, binding-allocated workspace), the two-call path
-(flexq_quant_act, then flexq_gemm_w6ax) and the split-K GEMM with one slice (its
-own workspace), and querying the automatic path, the prefill tile and the split-K
+(flexq_quant_act, then flexq_gemm_w6ax), the split-K GEMM with one slice (its
+own workspace) and, for A6, the packed pair (flexq_quant_act_a6_packed, then
+flexq_gemm_w6a6_packed), and querying the automatic path, the prefill tile and the split-K
 plan before every call, so the per-device compute-unit cache is first filled while
 the other threads use it.  The layers cover the decode kernel (1, 16
 and 40 rows) and the prefill kernel (300 rows), A6 and A8.  Every output must equal
@@ -63,11 +64,14 @@ def test_concurrent_threads_bit_exact(fq):
                     fq.auto_path(M, N, K)
                     fq.prefill_tile(M, N, K)
                     fq.splitk_plan(M, N, K)
-                    if it % 3 == 0:
+                    if it % 4 == 0:
                         outs.append(fq.linear_w6ax(x, wp, sw, N, abits))
-                    elif it % 3 == 1:
+                    elif it % 4 == 1:
                         qa, sa = fq.quant_act(x, abits)
                         outs.append(fq.gemm_w6ax(qa, sa, wp, sw, N, abits))
+                    elif it % 4 == 3 and abits == 6:  # 6-bit activation storage
+                        qp, sa = fq.quant_act_a6_packed(x)
+                        outs.append(fq.gemm_w6a6_packed(qp, sa, wp, sw, N))
                     else:  # split-K with one slice: the definition, bit for bit
                         qa, sa = fq.quant_act(x, abits)
                         outs.append(fq.gemm_w6ax_splitk(qa, sa, wp, sw, N, abits, splits=1,
