@@ -1,7 +1,7 @@
 /* Drives every function of the CPU oracle (oracle/flexq_oracle.c) on small seeded
  * inputs so that a build with -fsanitize=address,undefined sees every code path run:
  * the quantizers on ordinary, all-zero, extreme and subnormal groups, pack / unpack
- * of every code, the tiled packing of a matrix, group dots and the GEMM on one and
+ * of every code, the tiled packing of a matrix, the 6-bit activation storage, group dots and the GEMM on one and
  * several threads (with and without the optional accumulator outputs), and the
  * argument checks.  It also checks a few facts the oracle must keep (round trips,
  * thread-count independence) and exits non-zero on any mismatch; the sanitizers
@@ -110,6 +110,22 @@ int main(void) {
     CHECK(oracle_gemm_packed(qa, sa, wp, sw, M, N, K, G, yp, NULL, NULL, 300) == 0);
     CHECK(memcmp(y1, yp, sizeof(uint16_t) * M * N) == 0);
     for (int64_t i = 0; i < M * N; ++i) CHECK(s[i] >= 0.0);
+    if (abits == 6) { /* 6-bit activation storage: pack, unpack, round trip */
+      uint32_t* qp = malloc(sizeof(uint32_t) * 3 * M * K / 16);
+      int8_t* qa2 = malloc(M * K);
+      CHECK(qp && qa2);
+      CHECK(oracle_pack_act_a6(qa, M, K, qp) == 0);
+      CHECK(oracle_unpack_act_a6(qp, M, K, qa2) == 0);
+      CHECK(memcmp(qa, qa2, M * K) == 0);
+      free(qp);
+      free(qa2);
+    } else { /* A8 codes beyond 6 bits are refused */
+      uint32_t qp1[3 * K / 16];
+      int8_t row[K];
+      memset(row, 0, sizeof row);
+      row[5] = 127;
+      CHECK(oracle_pack_act_a6(row, 1, K, qp1) < 0);
+    }
   }
 
   /* argument checks return errors instead of touching memory */
@@ -117,6 +133,8 @@ int main(void) {
   CHECK(oracle_quant_w6(w, N, K + 1, G, qw, sw) < 0);
   CHECK(oracle_quant_act(x, M, K, G, 7, qa, sa) < 0);
   CHECK(oracle_pack_codes(qw, N + 1, K, wp) < 0);
+  CHECK(oracle_pack_act_a6(qa, M, K + 1, wp) < 0);
+  CHECK(oracle_unpack_act_a6(NULL, M, K, qa) < 0);
   CHECK(oracle_gemm(qa, sa, qw, sw, 0, N, K, G, y1, NULL, NULL, 1) < 0);
   CHECK(oracle_group_dots(qa, qw, M, N, K, 0, dots, 1) < 0);
 
