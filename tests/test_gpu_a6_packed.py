@@ -113,9 +113,9 @@ def test_quant_packed_writes_stay_inside_the_outputs(fq):
 # (M, N, K) on 256 compute units: narrow short layers (single 16-column tiles; up to
 # 4 rows chunks of 1 or 2 items, from 5 rows chunks of 1, 2 or 4), more than 2 single
 # tiles per CU (paired tiles, chunks of 2), deep K or wide N (paired tiles, 16 waves
-# up to 4 rows, 8 waves from 5, chunks of 1, 2 or 8), 17-32 rows (single tiles in
-# chunks of 1 or 4; paired in chunks of 1 or 8), 33-48 and 49-64 rows (chunks of 1 or
-# 4), and two passes of 64 rows (chunks of 1 and 8)
+# up to 4 rows, 8 waves from 5, chunks of 1, 2 or 8), 17-32 rows (paired tiles in
+# chunks of 1, 2 or 8), 33-48 and 49-64 rows (chunks of 1 or 4), and two passes of
+# 64 rows (chunks of 1 and 8)
 GEMM_SHAPES = [(1, 256, 1024), (4, 400, 2048), (4, 4608, 1024), (5, 272, 1152),
                (16, 1024, 4096), (8, 4608, 1024), (16, 8704, 1024), (3, 8448, 1024),
                (2, 256, 16512), (9, 512, 16512), (16, 144, 17920), (12, 13312, 1024),

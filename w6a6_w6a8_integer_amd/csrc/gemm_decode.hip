@@ -507,12 +507,12 @@ static hipError_t launch_decode_any(const int8_t* qa, const float* sa, const uin
     return launch_decode_t<1, 2, 8, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
   }
   if (rows <= 32) {
-    // single tiles on narrow, short layers as above; then chunks of up to 4 items.
-    // Paired tiles take 8 waves: the register budget then allows chunks of 8 items
-    // (activation fragments shared 8 ways; 16 waves fit only 2) and the column-
-    // segment fold (70B gate_up at M = 24 / 32: 80 -> 67 / 90 -> 73 us).
-    if (N / 16 <= 3 * cu && K <= 16384)
-      return launch_decode_t<2, 1, 16, 2, 4, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
+    // Paired tiles with 8 waves on every layer: the register budget allows chunks of
+    // 8 items (activation fragments shared 8 ways; 16 waves fit only 2) and the
+    // column-segment fold (70B gate_up at M = 24 / 32: 80 -> 67 / 90 -> 73 us).  From
+    // 17 rows the narrow layers gain from it too (single 16-column tiles in chunks of
+    // up to 4, 16 waves: qkv M = 24 / 32 22.3 / 24.5 -> 20.9 / 23.2 us, o M = 24
+    // 15.6 -> 14.5 us, o M = 32 equal).
     return launch_decode_t<2, 2, 8, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
   }
   if (rows <= 48)
