@@ -8,7 +8,8 @@ K a multiple of 128 in 128..3072 (group counts below, at and past the 16 a decod
 workgroup folds per round and the 6 a prefill loop unrolls), the activation
 precision and the path (automatic, decode, automatic prefill tile, one named tile,
 the warp-specialized kernel or the 64 x 128 tile).  Y and the activation codes and
-scales must equal the oracle's bit for bit.
+scales must equal the oracle's bit for bit; A6 cases also run the packed pair
+(flexq_quant_act_a6_packed, flexq_gemm_w6a6_packed) against the oracle's packing and Y.
 """
 import numpy as np
 import pytest
@@ -59,10 +60,17 @@ def test_random_shape_bit_exact(fq, i, M, N, K, abits, path):
     qw_ref, sw_ref = oracle.quant_w6(w)
     y_ref = oracle.gemm(qa_ref, sa_ref, qw_ref, sw_ref).view(np.uint16)
     wp, sw = fq.pack_w6(torch.from_numpy(w).to(DEV))
-    qa, sa = fq.quant_act(torch.from_numpy(x).to(DEV), abits)
+    xd = torch.from_numpy(x).to(DEV)
+    qa, sa = fq.quant_act(xd, abits)
     assert np.array_equal(qa.cpu().numpy(), qa_ref)
     assert np.array_equal(sa.cpu().numpy().T.view(np.uint32), sa_ref.view(np.uint32))
     y = fq.gemm_w6ax(qa, sa, wp, sw, N, abits, path=path)
     got = y.cpu().numpy().view(np.uint16)
     bad = np.argwhere(got != y_ref)
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+    if abits == 6:  # 6-bit activation storage: the oracle's packing and the same Y
+        qp, sap = fq.quant_act_a6_packed(xd)
+        yp = fq.gemm_w6a6_packed(qp, sap, wp, sw, N)
+        assert np.array_equal(qp.cpu().numpy().view(np.uint32), oracle.pack_act_a6(qa_ref))
+        assert torch.equal(sap.view(torch.int32), sa.view(torch.int32))
+        assert np.array_equal(yp.cpu().numpy().view(np.uint16), y_ref)
