@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
       }
       // park dots 4d (row-major [row][col]) and this group's scales, s_w as s_w / 4
       // (exact), so the fold forms t = RN(d * s_w) as float(4d) * (s_w / 4); with PA
-      // as float(16d) * (s_w / 16), |16d| <= 16 * 128 * 31 * 32 < 2^24 being exact too
+      // as float(16d) * (s_w / 16), exact too: |16d| <= 16 * 128 * 32 * 32 = 2^21
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
