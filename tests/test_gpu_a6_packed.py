@@ -161,3 +161,23 @@ def test_quant_then_gemm_packed_equals_the_byte_path(fq):
         torch.cuda.synchronize()
         assert torch.equal(sap.view(torch.int32), sa.view(torch.int32))
         assert torch.equal(yp.view(torch.int16), yb.view(torch.int16))
+
+
+def test_gemm_packed_every_code(fq):
+    """Codes the quantizer never produces still decode as the unit encoding says: a
+    packed activation holding every code -32 .. 31, and a row of -32 throughout
+    (against weights whose every group holds a code of magnitude 31, its maximum),
+    gives the oracle's Y on those codes."""
+    M, N, K = 5, 272, 1024
+    rng = np.random.default_rng(35)
+    qa = rng.integers(-32, 32, (M, K)).astype(np.int8)
+    qa[0, :64] = np.arange(-32, 32)
+    qa[1] = -32
+    w = synth.weights(synth.derive_seed(35, "w"), N, K)
+    wp_ref, sw_ref = oracle.pack_w6(w)
+    sa_ref = (rng.random((M, K // G)) + 0.5).astype(np.float32) * np.float32(0.01)
+    y_ref = oracle.gemm_packed(qa, sa_ref, wp_ref, sw_ref, N)
+    y = fq.gemm_w6a6_packed(to_dev(oracle.pack_act_a6(qa).view(np.int32)), to_dev(gm(sa_ref)),
+                            to_dev(wp_ref.view(np.int32)), to_dev(gm(sw_ref)), N)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), y_ref.view(np.uint16))
