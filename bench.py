@@ -535,10 +535,17 @@ def main():
             roofline["frac_of_measured_peak"] = round(pre_all["tops"] / peaks["mfma_i8_tops"], 4)
             roofline["rescale_loop_tops"] = peaks["rescale_loop_tops"]
             roofline["frac_of_rescale_loop"] = round(pre_all["tops"] / peaks["rescale_loop_tops"], 4)
-    else:
+    elif dec_all:
         roofline = {"kernel": "gemm_decode_kernel", "bound": "hbm",
                     "achieved": round(dec_all["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(dec_all["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                    "timing": (f"median over runs of {args.reps} back-to-back launches between "
+                               "HIP events on the launch stream")}
+    else:  # every GEMM of the chosen shapes runs split over K
+        roofline = {"kernel": "gemm_prefill_kernel (split-K) + splitk_reduce_kernel",
+                    "bound": "mfma", "achieved": round(split_all["tops"], 1),
+                    "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                    "frac": round(split_all["tops"] / INT8_PEAK_TOPS, 4), "traffic": None,
                     "timing": (f"median over runs of {args.reps} back-to-back launches between "
                                "HIP events on the launch stream")}
     # the two target figures also as scalars of the roofline record
