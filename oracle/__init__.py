@@ -56,6 +56,8 @@ def _load():
         "oracle_quant_act": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
         "oracle_pack_act_a6": (ctypes.c_int, [_P, _I64, _I64, _P]),
         "oracle_unpack_act_a6": (ctypes.c_int, [_P, _I64, _I64, _P]),
+        "oracle_block_act": (ctypes.c_int, [_P, _I64, _I64, _P]),
+        "oracle_unblock_act": (ctypes.c_int, [_P, _I64, _I64, _P]),
         "oracle_group_dots": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_int]),
         "oracle_gemm": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P,
                                        ctypes.c_int]),
@@ -185,6 +187,25 @@ def pack_act_a6(qa: np.ndarray) -> np.ndarray:
     qp = np.zeros((M, 3 * K // 16), np.uint32)
     _check(_load().oracle_pack_act_a6(qa.ctypes.data, M, K, qp.ctypes.data), "pack_act_a6")
     return qp
+
+
+def block_act(qa: np.ndarray) -> np.ndarray:
+    """Codes qa int8 [M][K] -> int8 [ceil(M/16)*16*K] in 16-row blocks: block b, group
+    g, 64-deep half h, row r, byte c at b*16*K + g*2048 + h*1024 + r*64 + c (pad rows
+    hold zero codes)."""
+    qa = _c(qa, np.int8)
+    M, K = qa.shape
+    out = np.empty((M + 15) // 16 * 16 * K, np.int8)
+    _check(_load().oracle_block_act(qa.ctypes.data, M, K, out.ctypes.data), "block_act")
+    return out
+
+
+def unblock_act(blk: np.ndarray, M: int, K: int) -> np.ndarray:
+    blk = _c(blk, np.int8)
+    assert blk.size == (M + 15) // 16 * 16 * K
+    qa = np.empty((M, K), np.int8)
+    _check(_load().oracle_unblock_act(blk.ctypes.data, M, K, qa.ctypes.data), "unblock_act")
+    return qa
 
 
 def unpack_act_a6(qp: np.ndarray, K: int) -> np.ndarray:

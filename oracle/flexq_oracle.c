@@ -264,6 +264,31 @@ int oracle_unpack_act_a6(const uint32_t* qp, int64_t M, int64_t K, int8_t* qa) {
 }
 
 /* ------------------------------------------------------------------------- */
+/* Activation codes in 16-row blocks: a layout only, no arithmetic.           */
+/* ------------------------------------------------------------------------- */
+
+static int64_t block_offset(int64_t m, int64_t k, int64_t K) {
+  int64_t b = m / 16, r = m % 16, g = k / 128, h = (k % 128) / 64, c = k % 64;
+  return b * 16 * K + g * 2048 + h * 1024 + r * 64 + c;
+}
+
+int oracle_block_act(const int8_t* qa, int64_t M, int64_t K, int8_t* out) {
+  if (!qa || !out || M <= 0 || K <= 0 || K % 128) return -1;
+  int64_t Mp = (M + 15) / 16 * 16;
+  memset(out, 0, (size_t)(Mp * K));
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t k = 0; k < K; ++k) out[block_offset(m, k, K)] = qa[m * K + k];
+  return 0;
+}
+
+int oracle_unblock_act(const int8_t* blk, int64_t M, int64_t K, int8_t* qa) {
+  if (!qa || !blk || M <= 0 || K <= 0 || K % 128) return -1;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t k = 0; k < K; ++k) qa[m * K + k] = blk[block_offset(m, k, K)];
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Integer group dots and the fused-dequantization accumulation               */
 /* Blog "Bridging ... BTC": exact integer partial products per K-group, then  */
 /* dequantization fused into the accumulation.                                */

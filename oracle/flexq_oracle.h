@@ -67,6 +67,14 @@ int oracle_pack_act_a6(const int8_t* qa, int64_t M, int64_t K, uint32_t* qp);
 /* Decode qp back into codes [M][K]. */
 int oracle_unpack_act_a6(const uint32_t* qp, int64_t M, int64_t K, int8_t* qa);
 
+/* Activation codes in 16-row blocks (the order the weight-streaming kernel feeds its
+   MFMAs): rows padded with zero codes to a multiple of 16; block b = m / 16, group g,
+   64-deep half h of the group, row r = m % 16 and byte c of the half at
+   b*16*K + g*2048 + h*1024 + r*64 + c.  K % 128 == 0.  out: ceil(M/16)*16*K bytes. */
+int oracle_block_act(const int8_t* qa, int64_t M, int64_t K, int8_t* out);
+/* The inverse on the first M rows. */
+int oracle_unblock_act(const int8_t* blk, int64_t M, int64_t K, int8_t* qa);
+
 /* Integer group dot products d[m][n][g] = sum over k in group g of qa[m][k]*qw[n][k]. */
 int oracle_group_dots(const int8_t* qa, const int8_t* qw, int64_t M, int64_t N, int64_t K,
                       int64_t group, int32_t* dots, int nthreads);

@@ -110,6 +110,22 @@ int main(void) {
     CHECK(oracle_gemm_packed(qa, sa, wp, sw, M, N, K, G, yp, NULL, NULL, 300) == 0);
     CHECK(memcmp(y1, yp, sizeof(uint16_t) * M * N) == 0);
     for (int64_t i = 0; i < M * N; ++i) CHECK(s[i] >= 0.0);
+    { /* codes in 16-row blocks: round trip, pad rows zero */
+      const int64_t Mp = (M + 15) / 16 * 16;
+      int8_t* blk = malloc(Mp * K);
+      int8_t* back = malloc(M * K);
+      CHECK(blk && back);
+      CHECK(oracle_block_act(qa, M, K, blk) == 0);
+      CHECK(oracle_unblock_act(blk, M, K, back) == 0);
+      CHECK(memcmp(qa, back, M * K) == 0);
+      int64_t nz = 0;
+      for (int64_t i = 0; i < Mp * K; ++i) nz += blk[i] != 0;
+      int64_t nzq = 0;
+      for (int64_t i = 0; i < M * K; ++i) nzq += qa[i] != 0;
+      CHECK(nz == nzq);
+      free(blk);
+      free(back);
+    }
     if (abits == 6) { /* 6-bit activation storage: pack, unpack, round trip */
       uint32_t* qp = malloc(sizeof(uint32_t) * 3 * M * K / 16);
       int8_t* qa2 = malloc(M * K);
@@ -135,6 +151,7 @@ int main(void) {
   CHECK(oracle_pack_codes(qw, N + 1, K, wp) < 0);
   CHECK(oracle_pack_act_a6(qa, M, K + 1, wp) < 0);
   CHECK(oracle_unpack_act_a6(NULL, M, K, qa) < 0);
+  CHECK(oracle_block_act(qa, M, K + 16, (int8_t*)wp) < 0);
   CHECK(oracle_gemm(qa, sa, qw, sw, 0, N, K, G, y1, NULL, NULL, 1) < 0);
   CHECK(oracle_group_dots(qa, qw, M, N, K, 0, dots, 1) < 0);
 

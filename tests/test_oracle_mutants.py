@@ -40,6 +40,8 @@ MUTANTS = [
      "oracle_pack_unit(qa + m * K + u * 16, qp + 3 * (u * M + m));"),
     ("act_a6_accepts_8bit_codes", "if (qa[i] < -32 || qa[i] > 31) return -3;",
      "if (qa[i] < -128 || qa[i] > 127) return -3;"),
+    ("block_rows_outside_halves", "return b * 16 * K + g * 2048 + h * 1024 + r * 64 + c;",
+     "return b * 16 * K + g * 2048 + r * 128 + h * 64 + c;"),
 ]
 
 PIN_TESTS = [
@@ -63,6 +65,8 @@ PIN_TESTS = [
     (pins.test_pack_act_a6_golden_units_in_row_order, {}),
     (pins.test_pack_act_a6_is_the_weight_unit_grid_transposed, {}),
     (pins.test_pack_act_a6_round_trip_and_range, {}),
+    (pins.test_block_act_is_the_padded_reshape, {}),
+    (pins.test_block_act_places_one_code_by_hand, {}),
 ]
 
 

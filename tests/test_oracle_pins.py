@@ -199,6 +199,39 @@ def test_pack_act_a6_round_trip_and_range():
 
 
 # ---------------------------------------------------------------------------
+# activation codes in 16-row blocks (a layout: pinned to numpy and by hand)
+# ---------------------------------------------------------------------------
+
+def test_block_act_is_the_padded_reshape():
+    """The blocked layout equals numpy's view of the zero-padded [M][K] codes as
+    [block][row][group][half][byte] with the row axis moved inside the half."""
+    rng = np.random.default_rng(13)
+    for M, K in [(1, 128), (16, 256), (20, 384), (33, 1152)]:
+        qa = rng.integers(-127, 128, (M, K)).astype(np.int8)
+        Mp = (M + 15) // 16 * 16
+        pad = np.zeros((Mp, K), np.int8)
+        pad[:M] = qa
+        ref = pad.reshape(Mp // 16, 16, K // 128, 2, 64).transpose(0, 2, 3, 1, 4).reshape(-1)
+        blk = oracle.block_act(qa)
+        assert np.array_equal(blk, ref)
+        assert np.array_equal(oracle.unblock_act(blk, M, K), qa)
+
+
+def test_block_act_places_one_code_by_hand():
+    # row 17, column 200 of a 20 x 256 matrix: block 1, row 1 in it, group 1, second
+    # half of the group (200 - 128 = 72 >= 64), byte 8 of it:
+    # 1*16*256 + 1*2048 + 1*1024 + 1*64 + 8 = 7240
+    qa = np.zeros((20, 256), np.int8)
+    qa[17, 200] = -77
+    blk = oracle.block_act(qa)
+    assert blk.size == 32 * 256
+    assert np.flatnonzero(blk).tolist() == [7240] and blk[7240] == -77
+    qa[:] = 5                                # every real code; the 12 pad rows stay zero
+    blk = oracle.block_act(qa)
+    assert int(np.count_nonzero(blk)) == 20 * 256
+
+
+# ---------------------------------------------------------------------------
 # quantizers
 # ---------------------------------------------------------------------------
 
