@@ -7,7 +7,9 @@ o 8192x8192, gate_up 57344x8192, down 8192x28672), quantize the fp16 activations
 (flexq_quant_act) and run the W6Ax GEMM on packed 6-bit weights resident in HBM:
 flexq_gemm_w6ax with its automatic kernel choice, or flexq_gemm_w6ax_splitk in the
 planned configuration where flexq_gemm_w6ax_splitk_plan cuts K into slices (mid-sized
-M on the narrow layers).  Weights are packed once, before timing (offline step).
+M on the narrow layers); where the choice is the weight-streaming kernel the codes are
+quantized into and read from 16-row blocks (flexq_quant_act_blocked,
+flexq_gemm_w6ax_blocked).  Weights are packed once, before timing (offline step).
 
 Prints one JSON line: value = whole-step GEMM+quant throughput in TOPS (2*M*N*K
 integer ops per GEMM, M unpadded), per-shape TOPS / GB/s / roofline fractions,
@@ -309,10 +311,13 @@ def main():
             x = synth.activations(synth.derive_seed(args.seed, "70b", name, "x", M), M, K,
                                   nthreads=nthreads)
             xd = torch.from_numpy(x).to(dev)
-            qa = torch.empty((M, K), dtype=torch.int8, device=dev)
+            kind = gemm_kind(fq, M, N, K)
+            # the streaming kernel's shapes keep their codes in 16-row blocks
+            qa = (torch.empty(fq.blocked_act_bytes(M, K), dtype=torch.int8, device=dev)
+                  if kind[0] == "decode" else
+                  torch.empty((M, K), dtype=torch.int8, device=dev))
             sa = torch.empty((K // GROUP, M), dtype=torch.float32, device=dev)
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
-            kind = gemm_kind(fq, M, N, K)
             ws = (torch.empty(fq.splitk_workspace_bytes(M, N, K, kind[1]), dtype=torch.uint8,
                               device=dev) if kind[0] == "splitk" else None)
             bufs[(M, name)] = (x, xd, qa, sa, y, kind, ws)
@@ -334,6 +339,15 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in plan]
 
+    def quant(M, name, ab):
+        """The activation quantization of one GEMM: into 16-row blocks for the streaming
+        kernel, row-major for the others."""
+        _, xd, qa, sa, _, kind, _ = bufs[(M, name)]
+        if kind[0] == "decode":
+            fq.quant_act_blocked(xd, ab, q_a_blk=qa, s_a=sa)
+        else:
+            fq.quant_act(xd, ab, q_a=qa, s_a=sa)
+
     def gemm(M, name, ab, wp, sw):
         """One GEMM of the step, as gemm_kind says it runs."""
         N, K = LAYERS[name]
@@ -341,16 +355,17 @@ def main():
         if kind[0] == "splitk":
             fq.gemm_w6ax_splitk(qa, sa, wp, sw, N, ab, splits=kind[1], path=kind[2], y=y,
                                 workspace=ws)
+        elif kind[0] == "decode":
+            fq.gemm_w6ax_blocked(qa, sa, wp, sw, N, ab, y=y)
         else:
             fq.gemm_w6ax(qa, sa, wp, sw, N, ab, y=y)
 
     def step(timed: bool):
         for i, (M, ab, name, widx) in enumerate(plan):
-            _, xd, qa, sa, y = bufs[(M, name)][:5]
             wp, sw = packed[name][widx]
             if timed:
                 ev[i][0].record()
-            fq.quant_act(xd, ab, q_a=qa, s_a=sa)
+            quant(M, name, ab)
             if timed:
                 ev[i][1].record()
             gemm(M, name, ab, wp, sw)
@@ -394,12 +409,11 @@ def main():
     for s in range(args.steps):
         for k in keys:
             M, ab, name = k
-            _, xd, qa, sa, y = bufs[(M, name)][:5]
             cps = packed[name]
             fq.peak_mfma_i8(80000, 0, sink, clock)
             r0.record()
             for j in range(REPS):
-                fq.quant_act(xd, ab, q_a=qa, s_a=sa)
+                quant(M, name, ab)
             r1.record()
             for j in range(REPS):
                 wp, sw = cps[(s * REPS + j) % len(cps)]
@@ -575,7 +589,8 @@ def main():
                    **({"stack_layers": STACK_LAYERS, "a8_layers": sorted(a8_layers)} if stack else {}),
                    "layers": {k: list(v) for k, v in LAYERS.items()}, "M": list(m_list),
                    "abits": list(ABITS), "group": GROUP,
-                   "step": "quant_act + gemm per (M, abits, layer); gemm = split-K where planned"},
+                   "step": ("quant_act + gemm per (M, abits, layer); gemm = split-K where "
+                            "planned; blocked codes for the streaming kernel")},
         "roofline": roofline, "cpu_baseline": cpu,
         "launch": "hip_graph" if graph_ms else "eager",
         "ms_per_step_eager": round(ms_per_step_eager, 3),

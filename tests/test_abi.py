@@ -150,6 +150,47 @@ def test_a6_packed_entry_points_reject_bad_arguments(flexq):
     assert call(N=0, wp=None, y=None) == SUCCESS
 
 
+def test_blocked_entry_points_reject_bad_arguments(flexq):
+    assert flexq.flexq_blocked_act_bytes(1, 128) == 16 * 128
+    assert flexq.flexq_blocked_act_bytes(17, 4096) == 32 * 4096
+    assert flexq.flexq_blocked_act_bytes(16, 100) == 0
+    assert flexq.flexq_blocked_act_bytes(0, 128) == 0
+    q = flexq.flexq_quant_act_blocked
+    assert q(A16, 4, 128, 128, 7, 2 * A16, 3 * A16, None) == INVALID
+    assert q(None, 4, 128, 128, 6, 2 * A16, 3 * A16, None) == INVALID
+    assert q(A16, 4, 128, 128, 6, None, 3 * A16, None) == INVALID
+    assert q(A16, 4, 128, 128, 6, 2 * A16, None, None) == INVALID
+    assert q(A16, -1, 128, 128, 6, 2 * A16, 3 * A16, None) == INVALID
+    assert q(A16, 4, 100, 128, 6, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert q(A16, 4, 128, 64, 6, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert q(A16 + 2, 4, 128, 128, 6, 2 * A16, 3 * A16, None) == UNSUPPORTED
+    assert q(A16, 4, 128, 128, 6, 2 * A16 + 8, 3 * A16, None) == UNSUPPORTED
+    assert q(A16, 4, 128, 128, 6, 2 * A16, 3 * A16 + 2, None) == UNSUPPORTED
+    assert q(A16, 4, 128, 128, 6, A16 + 512, 3 * A16, None) == INVALID      # codes inside x
+    # the codes take 16 rows (2048 bytes) even for 4: scales 2000 bytes in overlap them
+    assert q(A16, 4, 128, 128, 6, 2 * A16, 2 * A16 + 2000, None) == INVALID
+    assert q(None, 0, 128, 128, 6, None, None, None) == SUCCESS
+    g = flexq.flexq_gemm_w6ax_blocked
+    args = dict(qb=A16, sa=2 * A16, wp=3 * A16, sw=4 * A16, y=5 * A16)
+
+    def call(M=4, N=16, K=128, group=128, abits=8, **kw):
+        a = {**args, **kw}
+        return g(a["qb"], a["sa"], a["wp"], a["sw"], M, N, K, group, abits, a["y"], None)
+
+    for k in args:
+        assert call(**{k: None}) == INVALID, k
+    assert call(abits=5) == INVALID
+    assert call(M=-1) == INVALID
+    assert call(K=0) == INVALID
+    assert call(K=130) == UNSUPPORTED
+    assert call(N=24) == UNSUPPORTED
+    assert call(qb=A16 + 4) == UNSUPPORTED
+    assert call(y=5 * A16 + 2) == UNSUPPORTED
+    assert call(y=A16 + 1024) == INVALID      # Y overlaps the 16-row block of codes
+    assert call(M=0, qb=None, y=None) == SUCCESS
+    assert call(N=0, wp=None, y=None) == SUCCESS
+
+
 def test_gemm_rejects_bad_arguments(flexq):
     f = flexq.flexq_gemm_w6ax
     g = flexq.flexq_gemm_w6ax_path
@@ -194,9 +235,14 @@ def test_group_dots_rejects_bad_arguments(flexq):
 
 def test_linear_workspace_bytes(flexq):
     f = flexq.flexq_linear_w6ax_workspace_bytes
-    assert f(1, 128) == 256 + 4         # q_a 128 B rounded up to 256, then s_a
-    assert f(5, 128) == 768 + 5 * 4
-    assert f(3, 8192) == 24576 + 3 * 64 * 4
+    # up to 64 rows the codes take whole 16-row blocks (the streaming kernel's layout)
+    assert f(1, 128) == 16 * 128 + 4
+    assert f(5, 128) == 16 * 128 + 5 * 4
+    assert f(3, 8192) == 16 * 8192 + 3 * 64 * 4
+    assert f(17, 384) == 32 * 384 + 17 * 3 * 4
+    assert f(64, 8192) == 64 * 8192 + 64 * 64 * 4
+    # above, M * K row-major codes rounded up to 256 bytes
+    assert f(65, 128) == (65 * 128 + 255) // 256 * 256 + 65 * 4
     assert f(4096, 8192) == 4096 * 8192 + 4096 * 64 * 4
     assert f(0, 128) == 0 and f(-3, 128) == 0 and f(8, 100) == 0 and f(8, 0) == 0
 
@@ -370,6 +416,24 @@ def test_binding_checks_the_other_entry_points():
         fq.gemm_w6a6_packed(qp, sa, wp, sw, 32, y=torch.zeros(2, 16, dtype=f16))
     with pytest.raises(TypeError, match="CUDA"):
         fq.gemm_w6a6_packed(qp, sa, wp, sw, 32)
+    # blocked activation codes: int8, 1-D, ceil(M/16)*16*K bytes; M and K from s_a
+    with pytest.raises(ValueError, match="q_a_blk holds"):
+        fq.quant_act_blocked(x, 6, q_a_blk=torch.zeros(2 * 256, dtype=i8))
+    with pytest.raises(ValueError, match="q_a_blk must be 1-D"):
+        fq.quant_act_blocked(x, 6, q_a_blk=torch.zeros(16, 256, dtype=i8))
+    with pytest.raises(TypeError, match="CUDA"):
+        fq.quant_act_blocked(x, 6)
+    qb = torch.zeros(16 * 256, dtype=i8)
+    with pytest.raises(ValueError, match="q_a_blk holds"):
+        fq.gemm_w6ax_blocked(torch.zeros(15 * 256, dtype=i8), sa, wp, sw, 32, 6)
+    with pytest.raises(TypeError, match="q_a_blk must be"):
+        fq.gemm_w6ax_blocked(qb.view(torch.uint8), sa, wp, sw, 32, 6)
+    with pytest.raises(ValueError, match="s_w must have shape"):
+        fq.gemm_w6ax_blocked(qb, sa, wp, torch.zeros(32, 2, dtype=f16), 32, 6)
+    with pytest.raises(ValueError, match="y must have shape"):
+        fq.gemm_w6ax_blocked(qb, sa, wp, sw, 32, 6, y=torch.zeros(32, 2, dtype=f16))
+    with pytest.raises(TypeError, match="CUDA"):
+        fq.gemm_w6ax_blocked(qb, sa, wp, sw, 32, 6)
 
 
 def test_auto_path_rule(flexq):

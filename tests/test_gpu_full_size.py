@@ -18,9 +18,10 @@ order of the definition.  Where the split-K plan cuts K into slices (mid-sized M
 narrow layers), flexq_gemm_w6ax_splitk runs in the planned configuration too and its
 whole Y and fp32 accumulator are checked against the tolerance for a changed
 summation order (tests/tolerance.py).  At M <= 64 the one-call layer (flexq_linear_w6ax) must
-also give the two-call result in full, and for A6 the packed activations
-(flexq_quant_act_a6_packed) and the streaming GEMM over them (flexq_gemm_w6a6_packed)
-are checked whole against the oracle's packing and Y.
+also give the two-call result in full, the codes in 16-row blocks
+(flexq_quant_act_blocked) and the streaming GEMM over them (flexq_gemm_w6ax_blocked)
+are checked whole against the oracle's blocking and Y, and for A6 so are the packed
+activations (flexq_quant_act_a6_packed) and the GEMM over them (flexq_gemm_w6a6_packed).
 
 Workloads: the toy W6A6 layer, LLaMA-2-7B W6A6 (M 1/16/128), LLaMA-2-13B W6A8
 (M 1/64/512), LLaMA-2-70B in W6A6 and W6A8 (M 1/16/64/256/1024/4096), the distinct
@@ -190,6 +191,19 @@ def test_full_size(fq, wname, lname):
                 if M <= FULL_Y_MAX_M:
                     y_lin = fq.linear_w6ax(xd, wp, sw, N, abits)
                     assert torch.equal(y_lin.view(torch.int16), y.view(torch.int16))
+                if M <= FULL_Y_MAX_M:
+                    # codes in 16-row blocks: the whole blocked tensor, and the whole Y of
+                    # the streaming kernel over it
+                    say(f"{wname} {lname}: M={M} abits={abits}: blocked activation codes")
+                    qb, sab = fq.quant_act_blocked(xd, abits)
+                    yb = fq.gemm_w6ax_blocked(qb, sab, wp, sw, N, abits)
+                    torch.cuda.synchronize()
+                    assert np.array_equal(qb.cpu().numpy(), oracle.block_act(qa_ref))
+                    assert torch.equal(sab.view(torch.int32), sa.view(torch.int32))
+                    yb_got = yb.cpu().numpy().view(np.uint16)
+                    assert np.array_equal(yb_got, y_ref.view(np.uint16)), first_diffs(
+                        yb_got, y_ref.view(np.uint16), lambda b: (int(b[0]), int(b[1])))
+                    del qb, sab, yb
                 if M <= FULL_Y_MAX_M and abits == 6:
                     # 6-bit activation storage: the whole packed tensor, and the whole Y
                     # of the streaming kernel over it

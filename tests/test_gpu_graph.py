@@ -213,3 +213,54 @@ def test_a6_packed_graph_replays_match_eager(fq):
             assert torch.equal(sa.view(torch.int32), se.view(torch.int32)), \
                 f"replay {rep} case {i}: scales"
             assert torch.equal(y.view(torch.int16), ye.view(torch.int16)), f"replay {rep} case {i}: y"
+
+
+def test_blocked_graph_replays_match_eager(fq):
+    """The blocked-code quantizer and the streaming GEMM over its output in one HIP
+    graph: every replay, between eager work that poisons codes, scales and Y, gives
+    the eager bits, and those equal the oracle's."""
+    cases = [(1, 512, 1024, 6), (17, 1040, 2048, 8), (64, 400, 1152, 6)]
+    bufs = []
+    for i, (M, N, K, abits) in enumerate(cases):
+        x = synth.activations(synth.derive_seed(25, "x", i), M, K)
+        w = synth.weights(synth.derive_seed(25, "w", i), N, K)
+        qa_ref, sa_ref = oracle.quant_act(x, abits)
+        wp_ref, sw_ref = oracle.pack_w6(w)
+        ref = (oracle.block_act(qa_ref), sa_ref,
+               oracle.gemm_packed(qa_ref, sa_ref, wp_ref, sw_ref, N))
+        wp, sw = fq.pack_w6(torch.from_numpy(w).to(DEV))
+        qb = torch.empty(fq.blocked_act_bytes(M, K), dtype=torch.int8, device=DEV)
+        sa = torch.empty((K // G, M), dtype=torch.float32, device=DEV)
+        y = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        bufs.append((N, abits, torch.from_numpy(x).to(DEV), wp, sw, qb, sa, y, ref))
+
+    def run():
+        for (N, abits, xd, wp, sw, qb, sa, y, _) in bufs:
+            fq.quant_act_blocked(xd, abits, q_a_blk=qb, s_a=sa)
+            fq.gemm_w6ax_blocked(qb, sa, wp, sw, N, abits, y=y)
+
+    run()
+    torch.cuda.synchronize()
+    for (N, abits, xd, wp, sw, qb, sa, y, (qb_ref, sa_ref, y_ref)) in bufs:
+        assert np.array_equal(qb.cpu().numpy(), qb_ref)
+        assert np.array_equal(sa.cpu().numpy().T.view(np.uint32), sa_ref.view(np.uint32))
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), y_ref.view(np.uint16))
+    eager = [(qb.clone(), sa.clone(), y.clone()) for (*_, qb, sa, y, _) in bufs]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for (*_, qb, sa, y, _) in bufs:
+            qb.fill_(-1)
+            sa.fill_(float("nan"))
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, ((*_, qb, sa, y, _), (qe, se, ye)) in enumerate(zip(bufs, eager)):
+            assert torch.equal(qb, qe), f"replay {rep} case {i}: codes"
+            assert torch.equal(sa.view(torch.int32), se.view(torch.int32)), \
+                f"replay {rep} case {i}: scales"
+            assert torch.equal(y.view(torch.int16), ye.view(torch.int16)), f"replay {rep} case {i}: y"

@@ -8,8 +8,9 @@ K a multiple of 128 in 128..3072 (group counts below, at and past the 16 a decod
 workgroup folds per round and the 6 a prefill loop unrolls), the activation
 precision and the path (automatic, decode, automatic prefill tile, one named tile,
 the warp-specialized kernel or the 64 x 128 tile).  Y and the activation codes and
-scales must equal the oracle's bit for bit; A6 cases also run the packed pair
-(flexq_quant_act_a6_packed, flexq_gemm_w6a6_packed) against the oracle's packing and Y.
+scales must equal the oracle's bit for bit; every case also runs the blocked-code pair
+(flexq_quant_act_blocked, flexq_gemm_w6ax_blocked) and A6 cases the packed pair
+(flexq_quant_act_a6_packed, flexq_gemm_w6a6_packed) against the oracle's layouts and Y.
 """
 import numpy as np
 import pytest
@@ -68,6 +69,12 @@ def test_random_shape_bit_exact(fq, i, M, N, K, abits, path):
     got = y.cpu().numpy().view(np.uint16)
     bad = np.argwhere(got != y_ref)
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+    # codes in 16-row blocks: the oracle's blocking and the same Y
+    qb, sab = fq.quant_act_blocked(xd, abits)
+    yb = fq.gemm_w6ax_blocked(qb, sab, wp, sw, N, abits)
+    assert np.array_equal(qb.cpu().numpy(), oracle.block_act(qa_ref))
+    assert torch.equal(sab.view(torch.int32), sa.view(torch.int32))
+    assert np.array_equal(yb.cpu().numpy().view(np.uint16), y_ref)
     if abits == 6:  # 6-bit activation storage: the oracle's packing and the same Y
         qp, sap = fq.quant_act_a6_packed(xd)
         yp = fq.gemm_w6a6_packed(qp, sap, wp, sw, N)

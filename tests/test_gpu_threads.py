@@ -4,7 +4,8 @@ once, each thread enqueueing on a stream of its own (default priority).
 Four threads start together and each runs one layer 16 times, rotating through the
 one-call path (flexq_linear_w6ax, binding-allocated workspace), the two-call path
 (flexq_quant_act, then flexq_gemm_w6ax), the split-K GEMM with one slice (its
-own workspace) and, for A6, the packed pair (flexq_quant_act_a6_packed, then
+own workspace), the blocked-code pair (flexq_quant_act_blocked, then
+flexq_gemm_w6ax_blocked) and, for A6, the packed pair (flexq_quant_act_a6_packed, then
 flexq_gemm_w6a6_packed), and querying the automatic path, the prefill tile and the split-K
 plan before every call, so the per-device compute-unit cache is first filled while
 the other threads use it.  The layers cover the decode kernel (1, 16
@@ -64,7 +65,10 @@ def test_concurrent_threads_bit_exact(fq):
                     fq.auto_path(M, N, K)
                     fq.prefill_tile(M, N, K)
                     fq.splitk_plan(M, N, K)
-                    if it % 4 == 0:
+                    if it % 8 == 5:  # codes in 16-row blocks and the streaming GEMM
+                        qb, sa = fq.quant_act_blocked(x, abits)
+                        outs.append(fq.gemm_w6ax_blocked(qb, sa, wp, sw, N, abits))
+                    elif it % 4 == 0:
                         outs.append(fq.linear_w6ax(x, wp, sw, N, abits))
                     elif it % 4 == 1:
                         qa, sa = fq.quant_act(x, abits)

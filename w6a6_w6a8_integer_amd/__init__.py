@@ -51,6 +51,10 @@ SIGNATURES = {
     "flexq_packed_a6_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "flexq_quant_act_a6_packed": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "flexq_gemm_w6a6_packed": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P]),
+    "flexq_blocked_act_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "flexq_quant_act_blocked": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _P, _P]),
+    "flexq_gemm_w6ax_blocked": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P,
+                                               _P]),
     "flexq_gemm_w6ax": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P]),
     "flexq_gemm_w6ax_path": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32,
                                             _P, _P]),
@@ -267,6 +271,57 @@ def gemm_w6a6_packed(q_a6p: torch.Tensor, s_a: torch.Tensor, w_packed: torch.Ten
     _check(lib().flexq_gemm_w6a6_packed(q_a6p.data_ptr(), s_a.data_ptr(), w_packed.data_ptr(),
                                         s_w.data_ptr(), M, N, K, GROUP, y.data_ptr(),
                                         _stream(q_a6p)), "flexq_gemm_w6a6_packed")
+    return y
+
+
+def blocked_act_bytes(M: int, K: int) -> int:
+    return int(lib().flexq_blocked_act_bytes(M, K))
+
+
+def quant_act_blocked(x: torch.Tensor, abits: int, q_a_blk: torch.Tensor | None = None,
+                      s_a: torch.Tensor | None = None):
+    """fp16 X[M][K] -> (q_a_blk int8[ceil(M/16)*16*K]: the codes in 16-row blocks, the
+    order the streaming GEMM feeds its MFMAs, s_a fp32[K/128][M]); the codes and
+    scales of quant_act(x, abits)."""
+    _matrix(x, torch.float16, "x")
+    M, K = x.shape
+    G = _groups(K, "quant_act_blocked")
+    nbytes = (M + 15) // 16 * 16 * K
+    if q_a_blk is None:
+        q_a_blk = torch.empty(max(1, nbytes), dtype=torch.int8, device=x.device)
+    if s_a is None:
+        s_a = torch.empty((G, M), dtype=torch.float32, device=x.device)
+    if isinstance(q_a_blk, torch.Tensor) and q_a_blk.dim() != 1:
+        raise ValueError(f"q_a_blk must be 1-D, got shape {tuple(q_a_blk.shape)}")
+    _tensor(q_a_blk, torch.int8, "q_a_blk", min_bytes=nbytes)
+    _tensor(s_a, torch.float32, "s_a", shape=(G, M))
+    _on_gpu(x=x, q_a_blk=q_a_blk, s_a=s_a)
+    _check(lib().flexq_quant_act_blocked(x.data_ptr(), M, K, GROUP, abits, q_a_blk.data_ptr(),
+                                         s_a.data_ptr(), _stream(x)), "flexq_quant_act_blocked")
+    return q_a_blk, s_a
+
+
+def gemm_w6ax_blocked(q_a_blk: torch.Tensor, s_a: torch.Tensor, w_packed: torch.Tensor,
+                      s_w: torch.Tensor, N: int, abits: int, y: torch.Tensor | None = None):
+    """Y fp16[M][N] from blocked activation codes (q_a_blk, from quant_act_blocked; M and
+    K come from s_a fp32[K/128][M]) and packed weights: the streaming kernel, the bits of
+    gemm_w6ax on the row-major codes."""
+    _matrix(s_a, torch.float32, "s_a")
+    G, M = s_a.shape
+    K = G * GROUP
+    N = _cols(N)
+    if isinstance(q_a_blk, torch.Tensor) and q_a_blk.dim() != 1:
+        raise ValueError(f"q_a_blk must be 1-D, got shape {tuple(q_a_blk.shape)}")
+    _tensor(q_a_blk, torch.int8, "q_a_blk", min_bytes=(M + 15) // 16 * 16 * K)
+    _packed(w_packed, N, K)
+    _tensor(s_w, torch.float16, "s_w", shape=(G, N))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=s_a.device)
+    _tensor(y, torch.float16, "y", shape=(M, N))
+    _on_gpu(q_a_blk=q_a_blk, s_a=s_a, w_packed=w_packed, s_w=s_w, y=y)
+    _check(lib().flexq_gemm_w6ax_blocked(q_a_blk.data_ptr(), s_a.data_ptr(), w_packed.data_ptr(),
+                                         s_w.data_ptr(), M, N, K, GROUP, abits, y.data_ptr(),
+                                         _stream(s_a)), "flexq_gemm_w6ax_blocked")
     return y
 
 

@@ -149,8 +149,17 @@ void* scratch_address() {
   return p;
 }
 
-// The one-call layer on validated arguments: quantize X into the workspace (q_a,
-// then s_a at the next 256-byte boundary), then the GEMM with the automatic choice.
+// Bytes of the one-call layer's code area: the blocked codes of the streaming kernel
+// (whole 16-row blocks) up to one 64-row pass, the row-major codes above.
+size_t linear_code_bytes(int64_t M, int64_t K) {
+  const int64_t rows = M <= flexq::kDecodeRowsPerPass ? (M + 15) / 16 * 16 : M;
+  return ((size_t)rows * (size_t)K + 255) / 256 * 256;
+}
+
+// The one-call layer on validated arguments: quantize X into the workspace (the codes,
+// then s_a at the next 256-byte boundary), then the GEMM with the automatic choice --
+// the streaming kernel on codes in 16-row blocks, or the tiled kernel on row-major
+// codes.
 flexq_status run_linear(const uint16_t* x_fp16, const uint32_t* w_packed,
                         const uint16_t* s_w_fp16, int64_t M, int64_t N, int64_t K, int32_t abits,
                         void* workspace, uint16_t* y_fp16, hipStream_t s) {
@@ -159,11 +168,14 @@ flexq_status run_linear(const uint16_t* x_fp16, const uint32_t* w_packed,
     return launched(flexq::launch_linear_decode_fused(x_fp16, M, K, qmax, w_packed, s_w_fp16, N,
                                                       y_fp16, s));
   int8_t* q_a = static_cast<int8_t*>(workspace);
-  float* s_a = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        ((size_t)M * (size_t)K + 255) / 256 * 256);
+  float* s_a =
+      reinterpret_cast<float*>(static_cast<char*>(workspace) + linear_code_bytes(M, K));
+  if (flexq::auto_gemm_path(M, N) == FLEXQ_PATH_DECODE) {
+    FLEXQ_TRY(launched(flexq::launch_quant_act_blocked(x_fp16, M, K, qmax, q_a, s_a, s)));
+    return launched(
+        flexq::launch_gemm_decode_blocked(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
+  }
   FLEXQ_TRY(launched(flexq::launch_quant_act(x_fp16, M, K, qmax, q_a, s_a, s)));
-  if (flexq::auto_gemm_path(M, N) == FLEXQ_PATH_DECODE)
-    return launched(flexq::launch_gemm_decode(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
   return launched(flexq::launch_gemm_prefill(q_a, s_a, w_packed, s_w_fp16, M, N, K, y_fp16, s));
 }
 
@@ -271,6 +283,56 @@ flexq_status flexq_gemm_w6a6_packed(const uint32_t* q_a6p, const float* s_a,
     return FLEXQ_ERROR_INVALID_VALUE;
   return launched(flexq::launch_gemm_decode_a6p(q_a6p, s_a, w_packed, s_w_fp16, M, N, K, y_fp16,
                                                 (hipStream_t)stream));
+}
+
+size_t flexq_blocked_act_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % kGroup != 0) return 0;
+  return (size_t)((M + 15) / 16 * 16) * (size_t)K;
+}
+
+flexq_status flexq_quant_act_blocked(const uint16_t* x_fp16, int64_t M, int64_t K,
+                                     int32_t group_size, int32_t abits, int8_t* q_a_blk,
+                                     float* s_a, void* stream) {
+  FLEXQ_TRY(check_m(M));
+  FLEXQ_TRY(check_k(K, group_size));
+  FLEXQ_TRY(check_scales(M, K));
+  if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
+  if (M == 0) return FLEXQ_SUCCESS;
+  if (!x_fp16 || !q_a_blk || !s_a) return FLEXQ_ERROR_INVALID_VALUE;
+  if (!aligned(x_fp16, 16) || !aligned(q_a_blk, 16) || !aligned(s_a, 4))
+    return FLEXQ_ERROR_UNSUPPORTED;
+  const Range in = range_of(x_fp16, (uint64_t)M * K * 2);
+  const Range oq = range_of(q_a_blk, flexq_blocked_act_bytes(M, K));
+  const Range os = range_of(s_a, (uint64_t)M * (K / kGroup) * 4);
+  if (overlap(in, oq) || overlap(in, os) || overlap(oq, os)) return FLEXQ_ERROR_INVALID_VALUE;
+  return launched(flexq::launch_quant_act_blocked(x_fp16, M, K, abits == 6 ? 31 : 127, q_a_blk,
+                                                  s_a, (hipStream_t)stream));
+}
+
+flexq_status flexq_gemm_w6ax_blocked(const int8_t* q_a_blk, const float* s_a,
+                                     const uint32_t* w_packed, const uint16_t* s_w_fp16,
+                                     int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                     int32_t abits, uint16_t* y_fp16, void* stream) {
+  FLEXQ_TRY(check_m(M));
+  FLEXQ_TRY(check_n(N));
+  FLEXQ_TRY(check_k(K, group_size));
+  FLEXQ_TRY(check_scales(M, K));
+  FLEXQ_TRY(check_scales(N, K));
+  if (abits != 6 && abits != 8) return FLEXQ_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return FLEXQ_SUCCESS;
+  if (!q_a_blk || !s_a || !w_packed || !s_w_fp16 || !y_fp16) return FLEXQ_ERROR_INVALID_VALUE;
+  if (!aligned(q_a_blk, 16) || !aligned(w_packed, 16) || !aligned(s_a, 4) ||
+      !aligned(s_w_fp16, 2) || !aligned(y_fp16, 4))
+    return FLEXQ_ERROR_UNSUPPORTED;
+  const uint64_t G = (uint64_t)(K / kGroup);
+  const Range o = range_of(y_fp16, (uint64_t)M * N * 2);
+  if (overlap(o, range_of(q_a_blk, flexq_blocked_act_bytes(M, K))) ||
+      overlap(o, range_of(s_a, (uint64_t)M * G * 4)) ||
+      overlap(o, range_of(w_packed, (uint64_t)N * K * 3 / 4)) ||
+      overlap(o, range_of(s_w_fp16, (uint64_t)N * G * 2)))
+    return FLEXQ_ERROR_INVALID_VALUE;
+  return launched(flexq::launch_gemm_decode_blocked(q_a_blk, s_a, w_packed, s_w_fp16, M, N, K,
+                                                    y_fp16, (hipStream_t)stream));
 }
 
 flexq_status flexq_gemm_w6ax_path(const int8_t* q_a, const float* s_a, const uint32_t* w_packed,
@@ -388,7 +450,7 @@ flexq_status flexq_gemm_w6ax_splitk(const int8_t* q_a, const float* s_a, const u
 
 size_t flexq_linear_w6ax_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0 || K % kGroup != 0) return 0;
-  return ((size_t)M * (size_t)K + 255) / 256 * 256 + (size_t)M * (size_t)(K / kGroup) * 4;
+  return linear_code_bytes(M, K) + (size_t)M * (size_t)(K / kGroup) * 4;
 }
 
 flexq_status flexq_linear_w6ax(const uint16_t* x_fp16, const uint32_t* w_packed,

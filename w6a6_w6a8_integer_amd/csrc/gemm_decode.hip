@@ -83,21 +83,30 @@ struct Cursor {
 
 }  // namespace
 
-// FQ: the activation quantization fused in front (one pass of up to 16 rows): the
-// workgroup quantizes fp16 X (x, qmax) once into LDS -- the same per-group rule and
-// helper as flexq_quant_act, so codes and scales are bit-identical -- and the
-// activation fragments and scales are read from there instead of q_a / s_a.
-// PA: qa holds A6 codes packed 16 per 3 dwords, the units of a row in order
-// (0.75 K bytes per row); each fragment is one 12-byte unit, unpacked like the
-// weights into bytes 4 * q_a, so the MFMA dots are 16 d and the fold scales by
-// s_w / 16 instead of s_w / 4 (both exact).
-template <int MT, int T, int S, int P, int C, bool FQ, bool PA>
+// Where the activation codes come from (AL):
+// kActBytes: q_a row-major, one byte per code.
+// kActFused: the activation quantization fused in front (one pass of up to 16 rows):
+//   the workgroup quantizes fp16 X (x, qmax) once into LDS -- the same per-group rule
+//   and helper as flexq_quant_act, so codes and scales are bit-identical -- and the
+//   activation fragments and scales are read from there instead of q_a / s_a.
+// kActPacked6: qa holds A6 codes packed 16 per 3 dwords, the units of a row in order
+//   (0.75 K bytes per row); each fragment is one 12-byte unit, unpacked like the
+//   weights into bytes 4 * q_a, so the MFMA dots are 16 d and the fold scales by
+//   s_w / 16 instead of s_w / 4 (both exact).
+// kActBlocked: qa holds the codes in 16-row blocks, each group's two 64-deep halves
+//   stored as the 16 rows' 64-byte segments in turn (rows padded to a multiple of
+//   16): a fragment load reads 1 KB in one piece, 8 whole 128-byte lines, where the
+//   row-major codes give 16 half-used lines, and that line traffic is what makes 16
+//   and more rows slower than a few.
+constexpr int kActBytes = 0, kActFused = 1, kActPacked6 = 2, kActBlocked = 3;
+
+template <int MT, int T, int S, int P, int C, int AL>
 __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint32_t* __restrict__ wp,
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ y, int ntiles16,
     int ntiles, int items, int per_wg, const uint16_t* __restrict__ x, int qmax) {
+  constexpr bool FQ = AL == kActFused, PA = AL == kActPacked6, BL = AL == kActBlocked;
   static_assert(!FQ || MT == 1, "the fused quantizer covers one pass of up to 16 rows");
-  static_assert(!(FQ && PA), "the fused quantizer keeps its codes in LDS");
   static_assert(P % 2 == 0, "slot parity must be static");
   constexpr int U = C > P ? C : P;  // steps per loop iteration: ring slot and item static
   static_assert(U % P == 0 && U % C == 0, "step unroll");
@@ -132,10 +141,14 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
   const int8_t* lq = lds_x;
   const float* lsc = reinterpret_cast<const float*>(lds_x + (fq_rows * K + 15) / 16 * 16);
 
-  // bytes per activation row, and per group and 64-deep k-block of a row
+  // bytes per activation row (a 16-row block is 16 rows), and the strides of a group
+  // and of a 64-deep k-block, and the lane's offset in them
   const uint32_t a_row = PA ? (uint32_t)K / 4u * 3u : (uint32_t)K;
-  constexpr uint32_t a_grp = PA ? 96u : 128u, a_blk = PA ? 48u : 64u;
-  const uint32_t a_lane_off = (uint32_t)(lane & 15) * a_row + (uint32_t)(lane >> 4) * (a_blk / 4u);
+  constexpr uint32_t a_grp = BL ? 2048u : (PA ? 96u : 128u);
+  constexpr uint32_t a_blk = BL ? 1024u : (PA ? 48u : 64u);
+  const uint32_t a_lane_off =
+      BL ? (uint32_t)(lane & 15) * 64u + (uint32_t)(lane >> 4) * 16u
+         : (uint32_t)(lane & 15) * a_row + (uint32_t)(lane >> 4) * (a_blk / 4u);
 
   // Loads of step c.  Out-of-range buffer loads return zero: rows past the pass and
   // groups >= G vanish; empty steps read from empty buffers.  The activation
@@ -144,8 +157,12 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
     const bool live = c.live(item_end);
     const int tile = live ? c.tile0 + c.i : 0;  // in units of COLS columns
     const int row0 = live ? c.pass * 64 : 0;
-    const int rows = live ? min(ROWS, M - row0) : 0;
+    // rows of the pass the activation buffer holds (blocked: padded to whole blocks)
+    const int rows = live ? min(ROWS, (BL ? (M + 15) / 16 * 16 : M) - row0) : 0;
     const auto ra = make_rsrc(qa + (size_t)row0 * a_row, (uint32_t)rows * a_row);
+    // blocked: a lane whose row is a pad row reads past the buffer instead (zero, and no
+    // memory traffic), as the row-major codes' lanes past M do
+    const int real_rows = live ? min(ROWS, M - row0) : 0;
     // scales are group-major (s_a[g][m] at g*M + m, s_w[g][n] at g*N + n); entries of
     // rows past the pass or columns past N are read but never used
     const auto rsa = make_rsrc(sa + row0, live ? (uint32_t)((size_t)G * M - row0) * 4u : 0u);
@@ -167,7 +184,9 @@ __global__ __launch_bounds__(64 * S) void gemm_decode_kernel(
       for (int ms = 0; ms < MT; ++ms) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const uint32_t off = a_lane_off + (uint32_t)(ms * 16) * a_row + g * a_grp + j * a_blk;
+          uint32_t off = a_lane_off + (uint32_t)(ms * 16) * a_row + g * a_grp + j * a_blk;
+          if constexpr (BL)
+            if (ms * 16 + (lane & 15) >= real_rows) off = 0x80000000u;
           if constexpr (PA)
             b.a[ms][j] = __builtin_amdgcn_raw_buffer_load_b96(ra, off, 0, 0);
           else
@@ -430,19 +449,19 @@ int auto_gemm_path(int64_t M, int64_t N) {
   return M >= 48 && prefill_tile(M, N) == kTile64x128 ? 2 : 1;
 }
 
-template <int MT, int T, int S, int P, int C, bool FQ = false, bool PA = false>
+template <int MT, int T, int S, int P, int C, int AL = kActBytes>
 static hipError_t launch_decode_c(const int8_t* qa, const float* sa, const uint32_t* wp,
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                   uint16_t* y, int64_t ntiles16, int64_t ntiles, int64_t items,
                                   int64_t per_wg, int64_t grid, hipStream_t stream,
                                   const uint16_t* x = nullptr, int qmax = 0) {
-  const size_t lds_x = FQ ? fused_quant_lds_bytes(M, K) : 0;
-  return launch_kernel_lds(gemm_decode_kernel<MT, T, S, P, C, FQ, PA>, dim3((unsigned)grid),
+  const size_t lds_x = AL == kActFused ? fused_quant_lds_bytes(M, K) : 0;
+  return launch_kernel_lds(gemm_decode_kernel<MT, T, S, P, C, AL>, dim3((unsigned)grid),
                            dim3(64 * S), lds_x, stream, qa, sa, wp, sw, (int)M, (int)N, (int)K, y,
                            (int)ntiles16, (int)ntiles, (int)items, (int)per_wg, x, qmax);
 }
 
-template <int MT, int T, int S, int P, int CMAX, bool FQ = false, bool PA = false>
+template <int MT, int T, int S, int P, int CMAX, int AL = kActBytes>
 static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint32_t* wp,
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                   uint16_t* y, hipStream_t stream, bool chunk_few_rows = false,
@@ -459,23 +478,23 @@ static hipError_t launch_decode_t(const int8_t* qa, const float* sa, const uint3
   // few token rows not worth the empty steps of a partial chunk, except where the
   // caller found it pays)
   if (M <= 4 && !chunk_few_rows)
-    return launch_decode_c<MT, T, S, P, 1, FQ, PA>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles,
+    return launch_decode_c<MT, T, S, P, 1, AL>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles,
                                                    items, per_wg, grid, stream, x, qmax);
   if (CMAX >= 8 && per_wg >= 5)
-    return launch_decode_c<MT, T, S, P, (CMAX >= 8 ? 8 : 1), FQ, PA>(
+    return launch_decode_c<MT, T, S, P, (CMAX >= 8 ? 8 : 1), AL>(
         qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items, per_wg, grid, stream, x, qmax);
   if (CMAX >= 4 && per_wg >= 3)
-    return launch_decode_c<MT, T, S, P, (CMAX >= 4 ? 4 : 1), FQ, PA>(
+    return launch_decode_c<MT, T, S, P, (CMAX >= 4 ? 4 : 1), AL>(
         qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items, per_wg, grid, stream, x, qmax);
   if (CMAX >= 2 && per_wg >= 2)
-    return launch_decode_c<MT, T, S, P, (CMAX >= 2 ? 2 : 1), FQ, PA>(
+    return launch_decode_c<MT, T, S, P, (CMAX >= 2 ? 2 : 1), AL>(
         qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles, items, per_wg, grid, stream, x, qmax);
-  return launch_decode_c<MT, T, S, P, 1, FQ, PA>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles,
+  return launch_decode_c<MT, T, S, P, 1, AL>(qa, sa, wp, sw, M, N, K, y, ntiles16, ntiles,
                                                  items, per_wg, grid, stream, x, qmax);
 }
 
-// The kernel configuration for an M x N x K product (PA: packed A6 activations).
-template <bool PA>
+// The kernel configuration for an M x N x K product, activations as AL says.
+template <int AL>
 static hipError_t launch_decode_any(const int8_t* qa, const float* sa, const uint32_t* wp,
                                     const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                     uint16_t* y, hipStream_t stream) {
@@ -492,19 +511,19 @@ static hipError_t launch_decode_any(const int8_t* qa, const float* sa, const uin
     // paired tiles, o 12.3 -> 11.3 us with chunks of single tiles).
     if (N / 16 <= 3 * cu && K <= 16384) {
       if (rows <= 4 && N / 16 > 2 * cu)
-        return launch_decode_t<1, 2, 16, 2, 2, false, PA>(qa, sa, wp, sw, M, N, K, y, stream,
+        return launch_decode_t<1, 2, 16, 2, 2, AL>(qa, sa, wp, sw, M, N, K, y, stream,
                                                           true);
       if (rows <= 4)
-        return launch_decode_t<1, 1, 16, 2, 2, false, PA>(qa, sa, wp, sw, M, N, K, y, stream,
+        return launch_decode_t<1, 1, 16, 2, 2, AL>(qa, sa, wp, sw, M, N, K, y, stream,
                                                           true);
-      return launch_decode_t<1, 1, 16, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
+      return launch_decode_t<1, 1, 16, 2, 8, AL>(qa, sa, wp, sw, M, N, K, y, stream);
     }
     // Paired tiles: 16 waves for up to 4 rows; from 5 rows 8 waves with the
     // column-segment fold (70B down at M = 16: 39 -> 36 us; 16 waves stay faster
     // at M = 1, where the fold is tiny and more waves keep more loads in flight).
     if (rows <= 4)
-      return launch_decode_t<1, 2, 16, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
-    return launch_decode_t<1, 2, 8, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
+      return launch_decode_t<1, 2, 16, 2, 8, AL>(qa, sa, wp, sw, M, N, K, y, stream);
+    return launch_decode_t<1, 2, 8, 2, 8, AL>(qa, sa, wp, sw, M, N, K, y, stream);
   }
   if (rows <= 32) {
     // Paired tiles with 8 waves on every layer: the register budget allows chunks of
@@ -513,24 +532,30 @@ static hipError_t launch_decode_any(const int8_t* qa, const float* sa, const uin
     // 17 rows the narrow layers gain from it too (single 16-column tiles in chunks of
     // up to 4, 16 waves: qkv M = 24 / 32 22.3 / 24.5 -> 20.9 / 23.2 us, o M = 24
     // 15.6 -> 14.5 us, o M = 32 equal).
-    return launch_decode_t<2, 2, 8, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
+    return launch_decode_t<2, 2, 8, 2, 8, AL>(qa, sa, wp, sw, M, N, K, y, stream);
   }
   if (rows <= 48)
-    return launch_decode_t<3, 2, 8, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
-  return launch_decode_t<4, 2, 8, 2, 8, false, PA>(qa, sa, wp, sw, M, N, K, y, stream);
+    return launch_decode_t<3, 2, 8, 2, 8, AL>(qa, sa, wp, sw, M, N, K, y, stream);
+  return launch_decode_t<4, 2, 8, 2, 8, AL>(qa, sa, wp, sw, M, N, K, y, stream);
 }
 
 hipError_t launch_gemm_decode(const int8_t* qa, const float* sa, const uint32_t* wp,
                               const uint16_t* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                               hipStream_t stream) {
-  return launch_decode_any<false>(qa, sa, wp, sw, M, N, K, y, stream);
+  return launch_decode_any<kActBytes>(qa, sa, wp, sw, M, N, K, y, stream);
 }
 
 hipError_t launch_gemm_decode_a6p(const uint32_t* qp, const float* sa, const uint32_t* wp,
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                   uint16_t* y, hipStream_t stream) {
-  return launch_decode_any<true>(reinterpret_cast<const int8_t*>(qp), sa, wp, sw, M, N, K, y,
-                                 stream);
+  return launch_decode_any<kActPacked6>(reinterpret_cast<const int8_t*>(qp), sa, wp, sw, M, N, K,
+                                        y, stream);
+}
+
+hipError_t launch_gemm_decode_blocked(const int8_t* qb, const float* sa, const uint32_t* wp,
+                                      const uint16_t* sw, int64_t M, int64_t N, int64_t K,
+                                      uint16_t* y, hipStream_t stream) {
+  return launch_decode_any<kActBlocked>(qb, sa, wp, sw, M, N, K, y, stream);
 }
 
 hipError_t launch_linear_decode_fused(const uint16_t* x, int64_t M, int64_t K, int qmax,
@@ -540,13 +565,13 @@ hipError_t launch_linear_decode_fused(const uint16_t* x, int64_t M, int64_t K, i
   const int64_t cu = device_cu_count();
   if (N / 16 <= 3 * cu && K <= 16384) {
     if (N / 16 > 2 * cu)
-      return launch_decode_t<1, 2, 16, 2, 2, true>(nullptr, nullptr, wp, sw, M, N, K, y, stream,
-                                                   true, x, qmax);
-    return launch_decode_t<1, 1, 16, 2, 2, true>(nullptr, nullptr, wp, sw, M, N, K, y, stream,
-                                                 true, x, qmax);
+      return launch_decode_t<1, 2, 16, 2, 2, kActFused>(nullptr, nullptr, wp, sw, M, N, K, y,
+                                                        stream, true, x, qmax);
+    return launch_decode_t<1, 1, 16, 2, 2, kActFused>(nullptr, nullptr, wp, sw, M, N, K, y,
+                                                      stream, true, x, qmax);
   }
-  return launch_decode_t<1, 2, 16, 2, 8, true>(nullptr, nullptr, wp, sw, M, N, K, y, stream,
-                                               false, x, qmax);
+  return launch_decode_t<1, 2, 16, 2, 8, kActFused>(nullptr, nullptr, wp, sw, M, N, K, y, stream,
+                                                    false, x, qmax);
 }
 
 }  // namespace flexq

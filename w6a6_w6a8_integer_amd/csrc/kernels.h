@@ -45,6 +45,17 @@ hipError_t launch_gemm_decode_a6p(const uint32_t* qp, const float* sa, const uin
                                   const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                                   uint16_t* y, hipStream_t stream);
 
+// Activation codes in 16-row blocks, the order the streaming kernel feeds its MFMAs:
+// block b = m / 16, group g, 64-deep half h, row m % 16 and byte c at
+// b*16*K + g*2048 + h*1024 + (m%16)*64 + c, rows padded with zero codes to a multiple
+// of 16.  The quantizer gives the codes and scales of launch_quant_act; the streaming
+// GEMM over them gives the bits of launch_gemm_decode on the row-major codes.
+hipError_t launch_quant_act_blocked(const uint16_t* x, int64_t M, int64_t K, int qmax,
+                                    int8_t* qb, float* sa, hipStream_t stream);
+hipError_t launch_gemm_decode_blocked(const int8_t* qb, const float* sa, const uint32_t* wp,
+                                      const uint16_t* sw, int64_t M, int64_t N, int64_t K,
+                                      uint16_t* y, hipStream_t stream);
+
 // launch_kernel with `lds_bytes` of dynamic LDS.
 template <typename... Params, typename... Args>
 hipError_t launch_kernel_lds(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds_bytes,

@@ -4,7 +4,8 @@
 // abstract: 6-bit weights everywhere, 6- or 8-bit activations per layer).
 //
 // The activation quantizer can also write A6 codes packed 16 per 3 dwords (the
-// weight unit, FlexQ abstract: W6A6 holds activations at 6 bits).
+// weight unit, FlexQ abstract: W6A6 holds activations at 6 bits), or the codes in
+// 16-row blocks in the order the weight-streaming kernel feeds its MFMAs.
 //
 // Both kernels are HBM-bound elementwise passes.  Arithmetic follows the
 // formulas of the public header exactly (IEEE division, round half to even),
@@ -59,19 +60,38 @@ __global__ __launch_bounds__(128) void pack_w6_kernel(const uint16_t* __restrict
 
 // Thread = 8 consecutive activations; 16 adjacent lanes (one DPP row) = one
 // 128-deep group.  blockIdx.x = token row, blockIdx.y = chunk of 2048 columns.
-// PACKED (A6 only): the codes of lanes 2i and 2i+1 form one 16-code unit, which
-// the even lane writes (12 bytes at unit (m, k0 / 16) of the row-major unit grid).
-template <bool PACKED>
+// kOutPackedA6: the codes of lanes 2i and 2i+1 form one 16-code unit, which the even
+// lane writes (12 bytes at unit (m, k0 / 16) of the row-major unit grid).
+// kOutBlocked: the grid covers M rounded up to 16 rows; row m's 8 codes go to block
+// m / 16, group g, half h, row m % 16, byte c at (m/16)*16*K + g*2048 + h*1024 +
+// (m%16)*64 + c, and the rows past M write zero codes (no scale).
+constexpr int kOutBytes = 0, kOutPackedA6 = 1, kOutBlocked = 2;
+
+template <int OUT>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int M,
                                                         int K, int qmax, int8_t* __restrict__ qa,
                                                         float* __restrict__ sa) {
   const int64_t m = blockIdx.x;
   const int k0 = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (k0 >= K) return;  // whole groups drop out together (K % 128 == 0)
+  if constexpr (OUT == kOutBlocked) {
+    const int64_t off = (m >> 4) * 16 * K + (k0 >> 7) * 2048 + ((k0 >> 6) & 1) * 1024 +
+                        (m & 15) * 64 + (k0 & 63);
+    if (m >= M) {  // a pad row of the last block (the whole workgroup)
+      *reinterpret_cast<u32x2*>(qa + off) = u32x2{0u, 0u};
+      return;
+    }
+    const u32x4 h = *reinterpret_cast<const u32x4*>(x + m * K + k0);
+    float s;
+    const u32x2 codes = quant8_row16(h, qmax, s);
+    *reinterpret_cast<u32x2*>(qa + off) = codes;
+    if ((threadIdx.x & 15) == 0) sa[(int64_t)(k0 >> 7) * M + m] = s;
+    return;
+  }
   const u32x4 h = *reinterpret_cast<const u32x4*>(x + m * K + k0);
   float s;
   const u32x2 codes = quant8_row16(h, qmax, s);
-  if constexpr (PACKED) {
+  if constexpr (OUT == kOutPackedA6) {
     // the partner lane is in the same group, so it is active whenever this one is
     const uint32_t p0 = (uint32_t)__shfl_xor((int)codes[0], 1);
     const uint32_t p1 = (uint32_t)__shfl_xor((int)codes[1], 1);
@@ -97,15 +117,22 @@ hipError_t launch_pack_w6(const uint16_t* w, int64_t N, int64_t K, uint32_t* wp,
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int qmax, int8_t* qa,
                             float* sa, hipStream_t stream) {
   dim3 grid((unsigned)M, (unsigned)((K + 2047) / 2048));
-  return launch_kernel(quant_act_kernel<false>, grid, dim3(256), stream, x, (int)M, (int)K, qmax,
-                       qa, sa);
+  return launch_kernel(quant_act_kernel<kOutBytes>, grid, dim3(256), stream, x, (int)M, (int)K,
+                       qmax, qa, sa);
 }
 
 hipError_t launch_quant_act_a6_packed(const uint16_t* x, int64_t M, int64_t K, uint32_t* qp,
                                       float* sa, hipStream_t stream) {
   dim3 grid((unsigned)M, (unsigned)((K + 2047) / 2048));
-  return launch_kernel(quant_act_kernel<true>, grid, dim3(256), stream, x, (int)M, (int)K, 31,
-                       reinterpret_cast<int8_t*>(qp), sa);
+  return launch_kernel(quant_act_kernel<kOutPackedA6>, grid, dim3(256), stream, x, (int)M,
+                       (int)K, 31, reinterpret_cast<int8_t*>(qp), sa);
+}
+
+hipError_t launch_quant_act_blocked(const uint16_t* x, int64_t M, int64_t K, int qmax,
+                                    int8_t* qb, float* sa, hipStream_t stream) {
+  dim3 grid((unsigned)((M + 15) / 16 * 16), (unsigned)((K + 2047) / 2048));
+  return launch_kernel(quant_act_kernel<kOutBlocked>, grid, dim3(256), stream, x, (int)M,
+                       (int)K, qmax, qb, sa);
 }
 
 }  // namespace flexq
