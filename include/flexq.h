@@ -184,10 +184,11 @@ flexq_status flexq_quant_act_blocked(const uint16_t* x_fp16, int64_t M, int64_t 
 
 /* The GEMM over blocked activation codes: the weight-streaming kernel of
    FLEXQ_PATH_DECODE with each MFMA fragment loaded as one contiguous kilobyte (whole
-   cache lines) instead of sixteen 64-byte row segments; 5-20 % faster than the
-   row-major codes at 16 to 64 tokens.  Y is bit-identical to flexq_gemm_w6ax on the
-   row-major codes.  Any M is accepted; it is meant for few tokens (M <=
-   FLEXQ_DECODE_MAX_M), since above that the weights are streamed once per 64 rows.
+   cache lines) instead of sixteen 64-byte row segments: on LLaMA-2-70B layers as fast
+   as the row-major codes at 1 to 4 tokens and 1-24 % faster from 8 to 64.  Y is
+   bit-identical to flexq_gemm_w6ax on the row-major codes.  Any M is accepted; it
+   is meant for few tokens (M <= FLEXQ_DECODE_MAX_M), since above that the weights
+   are streamed once per 64 rows.
      q_a_blk  flexq_blocked_act_bytes(M, K) bytes, 16-byte aligned (its pad rows may
               hold anything: they only meet outputs that are never written)
      s_a, w_packed, s_w_fp16, y_fp16 as for flexq_gemm_w6ax
