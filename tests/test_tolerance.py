@@ -34,3 +34,19 @@ def test_check_decisions():
     assert not tolerance.check(y2, ref, acc_ref + [1.1e-4, 0, 0, 0], acc_ref, S)[0]
     # exact agreement passes
     assert tolerance.check(ref, ref, acc_ref, acc_ref, S) == (True, 0, 0)
+
+
+def test_check_overflowed_outputs():
+    """An output that overflows fp16 agrees with the same infinity; a finite value or
+    the other infinity is judged by the fp32 sums alone."""
+    ref = h([np.inf, -np.inf, 1.0])
+    acc_ref = np.array([7e4, -7e4, 1.0])
+    S = np.array([7e4, 7e4, 1.0])
+    with np.errstate(all="raise"):
+        assert tolerance.check(ref, ref, acc_ref, acc_ref, S) == (True, 0, 0)
+    # 65504 against +inf: more than an ulp apart, passes only on the fp32 sums
+    y = h([65504.0, -np.inf, 1.0])
+    assert tolerance.check(y, ref, acc_ref, acc_ref, S)[:2] == (True, 1)
+    assert not tolerance.check(y, ref, acc_ref - [1.0, 0, 0], acc_ref, S)[0]
+    assert not tolerance.check(h([-np.inf, -np.inf, 1.0]), ref, acc_ref - [2e4, 0, 0],
+                               acc_ref, S)[0]

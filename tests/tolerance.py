@@ -26,9 +26,14 @@ def ulp16(y_bits):
 def check(y_gpu_bits, y_ref_bits, acc_gpu, acc_ref, S):
     """Returns (every output passes, outputs beyond one ulp, outputs whose fp32 sum is
     off by more than REL * S).  Arrays of one shape; y as fp16 bit patterns."""
-    yg = np.asarray(y_gpu_bits, np.uint16).view(np.float16).astype(np.float64)
-    yr = np.asarray(y_ref_bits, np.uint16).view(np.float16).astype(np.float64)
-    within_ulp = np.abs(yg - yr) <= ulp16(y_ref_bits)
+    gb = np.asarray(y_gpu_bits, np.uint16)
+    rb = np.asarray(y_ref_bits, np.uint16)
+    yg = gb.view(np.float16).astype(np.float64)
+    yr = rb.view(np.float16).astype(np.float64)
+    # equal bits agree (also where both overflowed to the same infinity, whose
+    # difference is not a number)
+    with np.errstate(invalid="ignore"):
+        within_ulp = (gb == rb) | (np.abs(yg - yr) <= ulp16(rb))
     acc_ok = np.abs(np.asarray(acc_gpu, np.float64) - np.asarray(acc_ref, np.float64)) <= \
         REL * np.asarray(S, np.float64)
     ok = within_ulp | acc_ok
