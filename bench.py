@@ -21,7 +21,8 @@ between HIP events (the GEMM rotating over weight copies so none is served from
 the Infinity Cache), medians and p10 / p90 over --steps runs.
 --summarize-trace DB turns a rocprofv3 kernel trace of such a run into the
 markdown tables kept under profiles/, with the same figures recomputed from the
-kernel durations.
+kernel durations.  --power SECONDS reports board power and shader clock (amd-smi)
+under the prefill GEMM and the on-device peak loops instead of running the step.
 """
 from __future__ import annotations
 
@@ -101,6 +102,11 @@ def parse():
                    help="also compare, at every M <= 64 and layer, the streaming GEMM over one "
                         "byte per A6 code with flexq_gemm_w6a6_packed over 6-bit codes, and the "
                         "two activation quantizers (key a6_packed)")
+    p.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+                   help="instead of the step: board power and shader clock (amd-smi) while "
+                        "the prefill GEMM (70B gate_up, M = 4096), the rescale loop, the "
+                        "MFMA-only loop and a plain HBM read each run back to back for "
+                        "SECONDS; one JSON line, then exit")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="first run one device-to-device copy of this many MiB (the known-size "
                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -261,6 +267,9 @@ def main():
         LAYERS = LAYERS_TP8
     fq.lib()
     dev = torch.device("cuda:0")
+    if args.power:
+        print(json.dumps(power_profile(fq, torch, dev, args.power, args.seed)), flush=True)
+        return
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -666,6 +675,104 @@ def a6_packed_ab(fq, torch, dev, bufs, packed, m_list, reps):
     cols = ["layer", "M", "us_bytes", "us_packed", "speedup"]
     return {"gemm_cols": cols + ["same_bits"], "gemm": gemm_rows, "quant_cols": cols,
             "quant": quant_rows}
+
+
+def read_smi_power():
+    """(socket power in W, mean gfx clock over the XCDs in MHz) from one
+    `amd-smi metric -p -c --json` call, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True,
+                           text=True, timeout=10)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    return parse_smi_power(r.stdout) if r.returncode == 0 else None
+
+
+def parse_smi_power(text):
+    """Socket power and mean gfx clock from amd-smi's metric JSON (first GPU), or None."""
+    try:
+        d = json.loads(text)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        watts = float(g["power"]["socket_power"]["value"])
+        clks = [float(v["clk"]["value"]) for k, v in g["clock"].items()
+                if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        return (watts, sum(clks) / len(clks)) if clks else None
+    except (ValueError, KeyError, IndexError, TypeError):
+        return None
+
+
+def summarize_power(samples, skip=2):
+    """Per phase: the median power and clock of its samples, the first `skip` dropped
+    (the readings lag a phase change by about a second).  samples: (phase, reading)."""
+    by = {}
+    for phase, rd in samples:
+        if rd is not None:
+            by.setdefault(phase, []).append(rd)
+    out = {}
+    for phase, rds in by.items():
+        core = rds[skip:] if len(rds) > skip + 2 else rds
+        out[phase] = {"watts_median": statistics.median(w for w, _ in core),
+                      "gfx_mhz_median": round(statistics.median(c for _, c in core), 1),
+                      "samples": len(core)}
+    return out
+
+
+def power_profile(fq, torch, dev, seconds, seed):
+    """Board power and shader clock while each of four kernels runs back to back for
+    `seconds`: the 256 x 128 prefill GEMM on the 70B gate_up layer at M = 4096 (A6,
+    the recipe's X and W), the rescale loop, the MFMA-only loop and a plain read of
+    1 GiB.  amd-smi is sampled from a thread of this process."""
+    import threading
+    N, K = LAYERS["gate_up"]
+    M = 4096
+    x = torch.from_numpy(synth.activations(synth.derive_seed(seed, "power", "x"), M, K)).to(dev)
+    w = torch.from_numpy(synth.weights(synth.derive_seed(seed, "power", "w"), N, K,
+                                       nthreads=synth.default_threads())).to(dev)
+    wp, sw = fq.pack_w6(w)
+    del w
+    qa, sa = fq.quant_act(x, 6)
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    sink = torch.empty(fq.peak_sink_bytes(), dtype=torch.uint8, device=dev)
+    clock = torch.zeros(2, dtype=torch.int64, device=dev)
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    phase = ["idle"]
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            samples.append((phase[0], read_smi_power()))
+            time.sleep(0.2)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(2.0)
+    runs = {}
+    for name, fn in (
+            ("prefill_gate_up_m4096",
+             lambda: fq.gemm_w6ax(qa, sa, wp, sw, N, 6, y=y, path=fq.PATH_PREFILL_256X128)),
+            ("rescale_loop", lambda: fq.peak_mfma_i8_rescale(2000, sink, clock)),
+            ("mfma_loop", lambda: fq.peak_mfma_i8(20000, 0, sink, clock)),
+            ("hbm_read_1gib", lambda: fq.peak_hbm_read(buf, sink))):
+        phase[0] = name
+        t0, n = time.time(), 0
+        while time.time() - t0 < seconds:
+            for _ in range(8):
+                fn()
+            n += 8
+            torch.cuda.synchronize()
+        runs[name] = {"launches": n, "seconds": round(time.time() - t0, 2)}
+        phase[0] = "after_" + name
+        time.sleep(1.0)
+    stop.set()
+    th.join()
+    phases = summarize_power(samples)
+    for name, r in runs.items():
+        phases.setdefault(name, {}).update(r)
+    return {"power": phases, "device": torch.cuda.get_device_properties(dev).gcnArchName,
+            "source": "amd-smi metric -p -c --json (socket_power, gfx_* clk)"}
 
 
 def measure_peaks(fq, torch, dev, layers):

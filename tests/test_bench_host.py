@@ -1,8 +1,9 @@
 """Host-side logic of bench.py, on the CPU: the algorithmic byte counts it divides by,
 the traffic record it reads from profiles/ (and drops once the prefill kernel's
-source changes), the single-GPU guard, and the kernel-trace summary that recomputes
+source changes), the single-GPU guard, the kernel-trace summary that recomputes
 the bench's figures from rocprofv3 kernel durations (run here on a synthetic trace
-database laid out like the per-kernel runs of the bench)."""
+database laid out like the per-kernel runs of the bench), and the reading of
+amd-smi's power and clock report."""
 import os
 import sqlite3
 import subprocess
@@ -95,3 +96,21 @@ def test_trace_summary_recomputes_the_figures(tmp_path, capsys):
     dec = 2 * bench.gemm_bytes(1, 8192, 8192) / ((11.5e3 + 12.5e3) * 1e-9) / 1e9
     assert f"decode at M <= 16: {dec:.1f} GB/s" in out
     assert "4 runs of 3 calls" not in out and "8 runs of 3 calls" in out
+
+
+def test_power_readings():
+    """amd-smi metric JSON -> (socket W, mean gfx clock); per-phase medians with the
+    lagging first readings of a phase dropped."""
+    import json
+    gfx = {f"gfx_{i}": {"clk": {"value": 1900 + 10 * i, "unit": "MHz"}} for i in range(8)}
+    doc = {"gpu_data": [{"gpu": 0, "power": {"socket_power": {"value": 1372, "unit": "W"}},
+                         "clock": {**gfx, "mem_0": {"clk": {"value": 2000, "unit": "MHz"}},
+                                   "fclk_0": {"clk": "N/A"}}}]}
+    assert bench.parse_smi_power(json.dumps(doc)) == (1372.0, 1935.0)
+    assert bench.parse_smi_power("not json") is None
+    assert bench.parse_smi_power(json.dumps({"gpu_data": []})) is None
+    samples = [("a", (300.0, 100.0)), ("a", (900.0, 2300.0))] + \
+        [("a", (1370.0 + i, 1940.0)) for i in range(5)] + [("b", None), ("b", (1000.0, 2400.0))]
+    out = bench.summarize_power(samples)
+    assert out["a"] == {"watts_median": 1372.0, "gfx_mhz_median": 1940.0, "samples": 5}
+    assert out["b"]["samples"] == 1 and out["b"]["watts_median"] == 1000.0
