@@ -285,8 +285,10 @@ size_t flexq_gemm_w6ax_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, i
 
 /* The slice count S and tile (written to *tile_path when it is not NULL) that
    flexq_gemm_w6ax_splitk takes for an M x N x K product on the current device when
-   asked to choose.  S = 1 means splitting is not expected to beat the tile grid
-   alone.  Never fails (degenerate shapes report 1 and FLEXQ_PATH_PREFILL_128X64). */
+   asked to choose.  S = 1 means splitting is not expected to pay: not against the
+   tile grid alone and, up to 64 tokens, not against the weight-streaming kernel on
+   blocked codes (flexq_gemm_w6ax_blocked), the faster choice there.  Never fails
+   (degenerate shapes report 1 and FLEXQ_PATH_PREFILL_128X64). */
 int32_t flexq_gemm_w6ax_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t* tile_path);
 
 /* Bytes of workspace flexq_linear_w6ax needs for an M x K activation: the codes

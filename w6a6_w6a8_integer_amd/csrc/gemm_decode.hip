@@ -437,6 +437,26 @@ size_t fused_quant_lds_bytes(int64_t M, int64_t K) {
   return (size_t)((rows * K + 15) / 16 * 16 + rows * (K / kGroup) * 4);
 }
 
+// Time model of the weight-streaming kernel on codes in 16-row blocks at 33 to 64
+// rows (its paired-tile, 8-wave forms), in microseconds, fitted to the LLaMA-2 7B,
+// 13B and 70B layers and their 8-way tensor-parallel shares on MI355X (20 launches
+// back to back, weights rotated through HBM): 4.3 plus, per group each workgroup
+// walks, 0.205 up to 48 rows and 0.005 more per row above; workgroups that own two
+// or more items share each round's activation fragments over a chunk (x 0.8); a grid
+// that leaves CUs idle gives each workgroup more of the HBM bandwidth (x (0.7 + 0.3 *
+// workgroups / CUs)).  Over 90 shapes at 33-64 rows the split plan this model informs
+// takes in total within 1 % of the best of the streaming kernel, split-K and the
+// tile grid per shape (its largest miss: 2 us on the 8-way share of 70B qkv).
+double predict_decode_us(int64_t M, int64_t N, int64_t G, int64_t cu) {
+  const int64_t items = (N + 31) / 32;  // paired 16-column tiles
+  const int64_t grid = std::min(items, cu);
+  const int64_t per_wg = (items + grid - 1) / grid;
+  double c = 0.205 + (M > 48 ? 0.005 * (double)(M - 48) : 0.0);
+  if (per_wg >= 2) c *= 0.8;
+  c *= 0.7 + 0.3 * (double)grid / (double)cu;
+  return 4.3 + (double)(per_wg * G) * c;
+}
+
 int auto_gemm_path(int64_t M, int64_t N) {
   // Up to one 64-row pass the streaming kernel is faster than the 128-row prefill
   // tiles on every LLaMA-2-70B layer (M = 64, weights cold: qkv 37.5 vs 38.8 us, o 27

@@ -760,8 +760,10 @@ void splitk_plan(int64_t M, int64_t N, int64_t K, int* tile, int* S) {
         *S = (int)s;
       }
     }
-  // split only for a predicted gain of a tenth or more
-  if (best == 0.0 || best * 1.1 > direct) {
+  // split only for a predicted gain of a tenth or more over the tile grid and, up to
+  // one 64-row pass, over the weight-streaming kernel
+  if (best == 0.0 || best * 1.1 > direct ||
+      (M <= kDecodeRowsPerPass && best * 1.1 > predict_decode_us(M, N, G, cu))) {
     *tile = prefill_tile(M, N);
     *S = 1;
   }

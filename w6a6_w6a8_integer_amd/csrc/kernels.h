@@ -127,4 +127,8 @@ int device_cu_count();
 // The kernel the automatic path runs for an M x N product: 1 = decode, 2 = prefill.
 int auto_gemm_path(int64_t M, int64_t N);
 
+// Predicted time (us) of the weight-streaming kernel on blocked codes for an
+// M x N product with G groups, 33 <= M <= 64, on `cu` compute units.
+double predict_decode_us(int64_t M, int64_t N, int64_t G, int64_t cu);
+
 }  // namespace flexq
