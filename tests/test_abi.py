@@ -589,3 +589,29 @@ def test_splitk_plan_rule(flexq):
                 assert tile == fq.prefill_tile(M, N, K)
     assert fq.splitk_plan(0, 16, 128) == (1, fq.PATH_PREFILL_128X64)
     assert fq.splitk_plan(64, 16, 128)[0] == 1           # one group: nothing to split
+
+
+def test_splitk_plan_weighs_the_streaming_kernel(flexq):
+    """At 33-64 tokens the plan splits only where split-K beat the weight-streaming
+    kernel on blocked codes when both were timed on MI355X (20 launches, rotating
+    weights; 256 CUs assumed without a GPU): the streaming kernel keeps the o-like
+    layers and the narrow layers up to 48 tokens, split-K takes the long-K layers and
+    70B qkv from 56 tokens."""
+    import w6a6_w6a8_integer_amd as fq
+    cases = {  # (N, K): {M: split?}
+        (10240, 8192): {48: False, 56: True, 64: True},      # 70B qkv
+        (8192, 8192): {33: False, 64: False},                # 70B o
+        (8192, 28672): {48: False, 56: True, 64: True},      # 70B down
+        (4096, 4096): {33: False, 64: False},                # 7B o
+        (12288, 4096): {64: False},                          # 7B qkv
+        (5120, 13824): {33: True, 64: True},                 # 13B down
+        (8192, 1024): {33: False, 64: False},                # 70B o, 8-way share
+        (8192, 3584): {64: False},                           # 70B down, 8-way share
+        (7168, 8192): {64: False},                           # 70B gate_up, 8-way share
+        (1280, 8192): {64: True},                            # 70B qkv, 8-way share
+        (16384, 4096): {40: False, 64: False},
+    }
+    for (N, K), want in cases.items():
+        for M, split in want.items():
+            S, _ = fq.splitk_plan(M, N, K)
+            assert (S > 1) == split, (N, K, M, S)
