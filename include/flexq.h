@@ -64,7 +64,9 @@
  * Preconditions: finite inputs; outputs must not overlap inputs; group_size == 128;
  * K a positive multiple of 128; N a multiple of 16; pointers aligned as stated.
  * The functions may be called from any thread.  Their only global state is a
- * per-device cache of the compute-unit count, filled on first use (atomically).
+ * per-device cache of the compute-unit count, filled on first use (atomically), and
+ * the staging array of flexq_linear_w6ax_noalloc (one per GPU, with its address
+ * cached per device the same way).
  */
 #ifndef FLEXQ_H
 #define FLEXQ_H
