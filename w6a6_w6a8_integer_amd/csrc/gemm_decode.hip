@@ -448,8 +448,8 @@ size_t fused_quant_lds_bytes(int64_t M, int64_t K) {
 // takes in total within 1 % of the best of the streaming kernel, split-K and the
 // tile grid per shape (its largest miss: 2 us on the 8-way share of 70B qkv).
 double predict_decode_us(int64_t M, int64_t N, int64_t G, int64_t cu) {
-  const int64_t items = (N + 31) / 32;  // paired 16-column tiles
-  const int64_t grid = std::min(items, cu);
+  const int64_t items = std::max<int64_t>(1, (N + 31) / 32);  // paired 16-column tiles
+  const int64_t grid = std::max<int64_t>(1, std::min(items, cu));
   const int64_t per_wg = (items + grid - 1) / grid;
   double c = 0.205 + (M > 48 ? 0.005 * (double)(M - 48) : 0.0);
   if (per_wg >= 2) c *= 0.8;
